@@ -1,0 +1,232 @@
+"""Benchmark of block-causal sink + sliding-window attention over a bounded KV cache.
+
+One step = one chunk-step of the stream: the 2 denoise-step attention calls of
+the chunk being generated, then the append of its clean K/V (with the
+automatic eviction of the oldest window chunk).  The cache is filled before
+timing, so every timed step is at steady state (Nkv = Lc + T (n_sink + W + 1)).
+
+Prints ONE JSON line.  `value` is attention TFLOP/s over the timed chunk-steps
+(algorithmic FLOP 4 H T Nkv D per call, visible keys only), `ms_per_step` the
+milliseconds per chunk-step.  `roofline` is for the attention kernel, timed with
+events around each launch on the launch stream; `cpu_baseline` is the CPU
+oracle on a bounded sample of the same call.
+
+    python bench.py [--steps K] [--warmup W] [--config 720p|mid|long] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synthetic  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBPS = 8000.0
+METRIC = "attention TFLOP/s + ms per 720p chunk-step; % of MI355X bf16 MFMA peak"
+KERNEL_SRC = os.path.join(ROOT, "block_causal_kv_amd", "csrc", "attention_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_720p_traffic.json")
+
+
+def workload_name(spec: synthetic.StreamSpec) -> str:
+    return ("%s-shaped stream: T=%d tokens/chunk, Lc=%d, H=%d, D=%d, W=%d + %d sink, %d attention "
+            "calls + 1 clean append per chunk-step, %s K/V" % (spec.name, spec.chunk_tokens,
+                                                              spec.cond_len, spec.heads, spec.head_dim,
+                                                              spec.window, spec.n_sink, spec.steps,
+                                                              spec.kv_dtype))
+
+
+def flop_per_call(spec: synthetic.StreamSpec) -> float:
+    return 4.0 * spec.heads * spec.chunk_tokens * spec.steady_kv_len() * spec.head_dim
+
+
+def bytes_per_call(spec: synthetic.StreamSpec) -> float:
+    """Algorithmic bytes of one call: Q and O once, every visible K/V row once."""
+    el = 2
+    kv_el = 1 if spec.kv_dtype == "fp8" else 2
+    return (2.0 * spec.heads * spec.chunk_tokens * spec.head_dim * el +
+            2.0 * spec.heads * spec.steady_kv_len() * spec.head_dim * kv_el)
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(config: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != kernel_sha() or t.get("config") != config:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(spec: synthetic.StreamSpec, budget_s: float = 12.0) -> dict:
+    """Time the oracle on one steady-state call (chunk c = n_sink + W, whose
+    concatenated sequence is exactly the resident set), one head at a time,
+    until about budget_s of work; scale to TFLOP/s."""
+    from oracle.stream import attend_chunk
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    c = spec.n_sink + spec.window
+    ck, cv = synthetic.cond_inputs(spec)
+    clean = {j: synthetic.chunk_inputs(spec, j, clean_only=True) for j in range(c)}
+    x = synthetic.chunk_inputs(spec, c)
+    nkv = spec.cond_len + (c + 1) * spec.chunk_tokens
+    assert nkv == spec.steady_kv_len()
+    done_heads = 0
+    t0 = time.perf_counter()
+    for h in range(spec.heads):
+        attend_chunk(c, x.q[0], x.k[0], x.v[0], lambda j: clean[j].k_clean, lambda j: clean[j].v_clean,
+                     ck, cv, spec.window, spec.n_sink, spec.scale, heads=[h])
+        done_heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flop = 4.0 * done_heads * spec.chunk_tokens * nkv * spec.head_dim
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "oracle (numpy fp64, explicit mask over [cond | chunks 0..%d]) on chunk %d, "
+                      "step 1, %d of %d heads, all %d query rows: %.1f s; ms per chunk-step "
+                      "equivalent %.0f" % (c, c, done_heads, spec.heads, spec.chunk_tokens, dt,
+                                           spec.steps * flop_per_call(spec) / (flop / dt) * 1e3)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="720p", choices=["720p", "mid", "long"])
+    ap.add_argument("--sets", type=int, default=4, help="distinct input sets cycled by step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: attention shards by heads with no exchange, so "
+              "N GPUs would each run this same kernel on H/N heads; no multi-GPU run is made.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from block_causal_kv_amd import KVCache
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+    spec = synthetic.SPECS[args.config]
+    H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
+    dev = torch.device("cuda", 0)
+
+    def dev_bf16(x):
+        bits = synthetic.bf16_bits(x).view(np.int16)
+        return torch.from_numpy(bits).to(dev).view(torch.bfloat16)
+
+    # ---- inputs resident in HBM before timing
+    ck, cv = synthetic.cond_inputs(spec)
+    sets = []
+    for i in range(args.sets):
+        x = synthetic.chunk_inputs(spec, i)
+        sets.append({"q": [dev_bf16(a) for a in x.q], "k": [dev_bf16(a) for a in x.k],
+                     "v": [dev_bf16(a) for a in x.v], "kc": dev_bf16(x.k_clean),
+                     "vc": dev_bf16(x.v_clean)})
+    out = torch.empty((H, T, D), dtype=torch.bfloat16, device=dev)
+    cache = KVCache(T, spec.window, spec.n_sink, spec.cond_len, H, D, spec.kv_dtype)
+    cache.set_condition(dev_bf16(ck), dev_bf16(cv))
+    stream = torch.cuda.current_stream()
+
+    def chunk_step(i, ev=None):
+        s = sets[i % len(sets)]
+        for st in range(spec.steps):
+            if ev is not None:
+                ev[0][st].record(stream)
+            cache.attention(s["q"][st], s["k"][st], s["v"][st], out=out, stream=stream)
+            if ev is not None:
+                ev[1][st].record(stream)
+        if ev is not None:
+            ev[2].record(stream)
+        cache.append_chunk(s["kc"], s["vc"], stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    # fill the cache so every measured step is at steady state
+    for i in range(spec.n_sink + spec.window):
+        chunk_step(i)
+    for i in range(args.warmup):
+        chunk_step(i)
+    torch.cuda.synchronize()
+    q = cache.query()
+    assert q["occupancy"] == spec.n_sink + spec.window
+
+    evs = [([torch.cuda.Event(enable_timing=True) for _ in range(spec.steps)],
+            [torch.cuda.Event(enable_timing=True) for _ in range(spec.steps)],
+            torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        chunk_step(i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    attn_ms = [e[0][s].elapsed_time(e[1][s]) for e in evs for s in range(spec.steps)]
+    app_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    ms_step = elapsed * 1e3 / args.steps
+    fl_call = flop_per_call(spec)
+    value = spec.steps * fl_call * args.steps / elapsed / 1e12
+    attn_avg = float(np.mean(attn_ms))
+    achieved = fl_call / (attn_avg * 1e-3) / 1e12
+    peak = PEAK_FP8_TFLOPS if spec.kv_dtype == "fp8" else PEAK_BF16_TFLOPS
+    traffic = measured_traffic(args.config)
+    app_bytes = 2.0 * 2 * H * T * D * (1 if spec.kv_dtype == "fp8" else 2)  # K+V read and written
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16; 1% of K rows x8)",
+        "config": {"workload": workload_name(spec), "chunk_tokens": T, "cond_len": spec.cond_len,
+                   "heads": H, "head_dim": D, "window": spec.window, "n_sink": spec.n_sink,
+                   "kv_len": spec.steady_kv_len(), "calls_per_step": spec.steps,
+                   "input_sets": args.sets},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "attention_ms_per_call": round(attn_avg, 4),
+        "attention_ms_p50_p99_max": [round(float(np.percentile(attn_ms, p)), 4) for p in (50, 99, 100)],
+        "append_ms": round(float(np.mean(app_ms)), 4),
+        "append_GBps": round(app_bytes / (float(np.mean(app_ms)) * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": bytes_per_call(spec),
+                     "algorithmic_flop_per_launch": fl_call},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(spec)
+    else:
+        rec["cpu_baseline"] = None
+    cache.close()
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,166 @@
+"""Block-causal sink + sliding-window attention over a bounded KV cache on MI355X.
+
+A thin binding of the C-ABI library ``libkvc.so`` (declared in ``include/kvc.h``):
+it checks tensor shapes/dtypes and passes device pointers and the current HIP
+stream.  Every step of the computation runs in the library's HIP kernels; there
+is no Python or CPU fallback, and loading fails if the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import List, Optional, Tuple
+
+from . import _lib
+from ._lib import KVCError, check, load
+
+__all__ = ["KVCache", "SlotTable", "KVCError", "load"]
+
+_DTYPES = {"bf16": _lib.KVC_KV_BF16, "fp8": _lib.KVC_KV_FP8}
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+class KVCache:
+    """Owner of one bounded KV cache (``kv_cache_create`` ... ``kv_cache_destroy``)."""
+
+    def __init__(self, chunk_tokens: int, window: int, n_sink: int = 1, cond_len: int = 0,
+                 heads: int = 1, head_dim: int = 128, kv_dtype: str = "bf16"):
+        self._lib = load()
+        self.T, self.W, self.n_sink, self.Lc = chunk_tokens, window, n_sink, cond_len
+        self.H, self.D, self.kv_dtype = heads, head_dim, kv_dtype
+        h = C.c_void_p()
+        check(self._lib.kv_cache_create(chunk_tokens, window, n_sink, cond_len, heads, head_dim,
+                                        _DTYPES[kv_dtype], C.byref(h)))
+        self._h = h
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value is not None:
+            check(self._lib.kv_cache_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    # ---- tensor checks (marshalling)
+    def _check(self, t, rows: int, name: str, dtype=None):
+        import torch
+        dtype = torch.bfloat16 if dtype is None else dtype
+        if t is None:
+            raise ValueError("%s is None" % name)
+        if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous %s CUDA tensor" % (name, dtype))
+        if tuple(t.shape) != (self.H, rows, self.D):
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (self.H, rows, self.D)))
+        return C.c_void_p(t.data_ptr())
+
+    def set_condition(self, k, v, stream=None) -> None:
+        if self.Lc == 0:
+            return
+        check(self._lib.kv_cache_set_condition(self._h, self._check(k, self.Lc, "k_cond"),
+                                               self._check(v, self.Lc, "v_cond"),
+                                               C.c_void_p(_stream_ptr(stream))))
+
+    def append_chunk(self, k, v, stream=None) -> Tuple[int, int, int]:
+        cid, slot, ev = C.c_int64(), C.c_int(), C.c_int64()
+        check(self._lib.kv_cache_append_chunk(self._h, self._check(k, self.T, "k"),
+                                              self._check(v, self.T, "v"),
+                                              C.c_void_p(_stream_ptr(stream)), C.byref(cid),
+                                              C.byref(slot), C.byref(ev)))
+        return cid.value, slot.value, ev.value
+
+    def evict(self, n: int) -> List[int]:
+        ids = (C.c_int64 * max(n, 1))()
+        cnt = C.c_int()
+        check(self._lib.kv_cache_evict(self._h, n, ids, C.byref(cnt)))
+        return [ids[i] for i in range(cnt.value)]
+
+    def reset(self) -> None:
+        check(self._lib.kv_cache_reset(self._h))
+
+    def query(self) -> dict:
+        nxt, occ = C.c_int64(), C.c_int()
+        n = self.n_sink + self.W
+        slots = (C.c_int64 * n)()
+        check(self._lib.kv_cache_query(self._h, C.byref(nxt), C.byref(occ), slots, n))
+        return {"next_chunk_id": nxt.value, "occupancy": occ.value, "slots": list(slots)}
+
+    def attention(self, q, k_cur, v_cur, out=None, lse=None, scale: float = 0.0, stream=None):
+        """Attention of the next chunk's queries; returns ``out`` ([H][T][D] bf16)."""
+        import torch
+        qp = self._check(q, self.T, "q")
+        kp = self._check(k_cur, self.T, "k_cur")
+        vp = self._check(v_cur, self.T, "v_cur")
+        if out is None:
+            out = torch.empty_like(q)
+        op = self._check(out, self.T, "out")
+        lp = None
+        if lse is not None:
+            if not lse.is_cuda or lse.dtype != torch.float32 or not lse.is_contiguous() \
+                    or tuple(lse.shape) != (self.H, self.T):
+                raise ValueError("lse must be a contiguous float32 CUDA tensor [H, T]")
+            lp = C.c_void_p(lse.data_ptr())
+        check(self._lib.sink_window_attention(self._h, qp, kp, vp, op, lp, C.c_float(scale),
+                                              C.c_void_p(_stream_ptr(stream))))
+        return out
+
+
+class SlotTable:
+    """Host-only slot table (``kvc_table_*``): the cache's index logic without a GPU."""
+
+    def __init__(self, window: int, n_sink: int = 1):
+        self._lib = load()
+        self.W, self.n_sink = window, n_sink
+        h = C.c_void_p()
+        check(self._lib.kvc_table_create(window, n_sink, C.byref(h)))
+        self._h = h
+
+    def __del__(self):
+        try:
+            if self._h is not None:
+                self._lib.kvc_table_destroy(self._h)
+                self._h = None
+        except Exception:
+            pass
+
+    def append(self) -> Tuple[int, int, int]:
+        cid, slot, ev = C.c_int64(), C.c_int(), C.c_int64()
+        check(self._lib.kvc_table_append(self._h, C.byref(cid), C.byref(slot), C.byref(ev)))
+        return cid.value, slot.value, ev.value
+
+    def evict(self, n: int) -> List[int]:
+        ids = (C.c_int64 * max(n, 1))()
+        cnt = C.c_int()
+        check(self._lib.kvc_table_evict(self._h, n, ids, C.byref(cnt)))
+        return [ids[i] for i in range(cnt.value)]
+
+    def reset(self) -> None:
+        check(self._lib.kvc_table_reset(self._h))
+
+    def query(self) -> dict:
+        nxt, occ = C.c_int64(), C.c_int()
+        n = self.n_sink + self.W
+        slots = (C.c_int64 * n)()
+        check(self._lib.kvc_table_query(self._h, C.byref(nxt), C.byref(occ), slots, n))
+        return {"next_chunk_id": nxt.value, "occupancy": occ.value, "slots": list(slots)}
+
+    def segments(self, chunk_tokens: int, cond_len: int, merge: bool = True):
+        cap = _lib.KVC_MAX_SLOTS + 2
+        r0 = (C.c_int32 * cap)()
+        ln = (C.c_int32 * cap)()
+        n = C.c_int()
+        check(self._lib.kvc_table_segments(self._h, chunk_tokens, cond_len, int(merge), r0, ln, cap,
+                                           C.byref(n)))
+        return [(r0[i], ln[i]) for i in range(n.value)]

@@ -1,0 +1,292 @@
+// C-ABI of the bounded KV cache and its block-causal sink + window attention.
+// Argument validation, the device pool, the host slot table and kernel launches.
+// Every check happens before anything is enqueued, and a failed call leaves
+// the cache state unchanged.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/kvc.h"
+#include "launch.h"
+#include "slot_table.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(KVC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+struct kvc_cache {
+  int T, W, n_sink, Lc, H, D, kv_dtype;
+  int device;
+  int64_t pool_rows;
+  void* k_pool = nullptr;  // [H][pool_rows][D] bf16 (fp8: bytes)
+  void* v_pool = nullptr;
+  kvc::SlotTable table;
+  int variant = 0;  // attention tiling (0 = default)
+  kvc_cache(int T_, int W_, int S_, int Lc_, int H_, int D_, int dt)
+      : T(T_), W(W_), n_sink(S_), Lc(Lc_), H(H_), D(D_), kv_dtype(dt), device(0),
+        pool_rows((int64_t)Lc_ + (int64_t)(S_ + W_) * T_), table(W_, S_) {}
+};
+
+struct kvc_table {
+  kvc::SlotTable table;
+  kvc_table(int W, int S) : table(W, S) {}
+};
+
+extern "C" {
+
+const char* kvc_last_error(void) { return g_last_error.c_str(); }
+
+int kv_cache_create(int chunk_tokens, int window_w, int n_sink, int cond_len, int heads,
+                    int head_dim, int kv_dtype, kvc_handle* out) {
+  g_last_error.clear();
+  if (!out) return fail(KVC_ERR_INVALID, "kv_cache_create: out is NULL");
+  if (chunk_tokens < 1 || window_w < 1 || n_sink < 0 || cond_len < 0 || heads < 1)
+    return fail(KVC_ERR_INVALID,
+                "kv_cache_create: need T >= 1, W >= 1, n_sink >= 0, Lc >= 0, H >= 1 "
+                "(got T=%d W=%d n_sink=%d Lc=%d H=%d)",
+                chunk_tokens, window_w, n_sink, cond_len, heads);
+  if (n_sink + window_w > KVC_MAX_SLOTS)
+    return fail(KVC_ERR_INVALID, "kv_cache_create: n_sink + W = %d exceeds %d", n_sink + window_w,
+                KVC_MAX_SLOTS);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(KVC_ERR_UNSUPPORTED, "kv_cache_create: head_dim %d not in {64, 128}", head_dim);
+  if (kv_dtype != KVC_KV_BF16)
+    return fail(KVC_ERR_UNSUPPORTED, "kv_cache_create: kv_dtype %d not supported", kv_dtype);
+  const int64_t pool_rows = (int64_t)cond_len + (int64_t)(n_sink + window_w) * chunk_tokens;
+  if (pool_rows > INT32_MAX || (int64_t)chunk_tokens * heads > INT32_MAX)
+    return fail(KVC_ERR_INVALID, "kv_cache_create: sizes overflow 32-bit row indices");
+  kvc_cache* c = new (std::nothrow) kvc_cache(chunk_tokens, window_w, n_sink, cond_len, heads,
+                                              head_dim, kv_dtype);
+  if (!c) return fail(KVC_ERR_OOM, "kv_cache_create: host allocation failed");
+  hipError_t e = hipGetDevice(&c->device);
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(e, "kv_cache_create: hipGetDevice");
+  }
+  const size_t elem = 2;
+  const size_t bytes = (size_t)heads * (size_t)pool_rows * (size_t)head_dim * elem;
+  e = hipMalloc(&c->k_pool, bytes);
+  if (e == hipSuccess) e = hipMalloc(&c->v_pool, bytes);
+  if (e != hipSuccess) {
+    if (c->k_pool) (void)hipFree(c->k_pool);
+    (void)hipGetLastError();
+    delete c;
+    return fail(e == hipErrorOutOfMemory ? KVC_ERR_OOM : KVC_ERR_HIP,
+                "kv_cache_create: hipMalloc of 2 x %zu bytes failed: %s", bytes, hipGetErrorString(e));
+  }
+  if (const char* v = getenv("KVC_ATTN_VARIANT")) c->variant = atoi(v);
+  *out = c;
+  return KVC_OK;
+}
+
+int kv_cache_destroy(kvc_handle h) {
+  g_last_error.clear();
+  if (!h) return KVC_OK;
+  int rc = KVC_OK;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) rc = hip_fail(e, "kv_cache_destroy: hipDeviceSynchronize");
+  if (h->k_pool) (void)hipFree(h->k_pool);
+  if (h->v_pool) (void)hipFree(h->v_pool);
+  delete h;
+  return rc;
+}
+
+int kv_cache_set_condition(kvc_handle h, const void* k_cond, const void* v_cond, void* stream) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "kv_cache_set_condition: handle is NULL");
+  if (h->Lc == 0) return KVC_OK;
+  if (!k_cond || !v_cond) return fail(KVC_ERR_INVALID, "kv_cache_set_condition: NULL K or V");
+  if (kvc::launch_pool_write_bf16((const uint16_t*)k_cond, (const uint16_t*)v_cond,
+                                  (uint16_t*)h->k_pool, (uint16_t*)h->v_pool, h->H, h->Lc, h->D,
+                                  h->pool_rows, 0, (hipStream_t)stream) != 0)
+    return fail(KVC_ERR_HIP, "kv_cache_set_condition: launch failed");
+  return KVC_OK;
+}
+
+int kv_cache_append_chunk(kvc_handle h, const void* k, const void* v, void* stream,
+                          int64_t* out_chunk_id, int* out_slot, int64_t* out_evicted) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "kv_cache_append_chunk: handle is NULL");
+  if (!k || !v) return fail(KVC_ERR_INVALID, "kv_cache_append_chunk: NULL K or V");
+  int slot;
+  int64_t evicted;
+  h->table.plan_append(&slot, &evicted);
+  const int row0 = h->Lc + slot * h->T;
+  if (kvc::launch_pool_write_bf16((const uint16_t*)k, (const uint16_t*)v, (uint16_t*)h->k_pool,
+                                  (uint16_t*)h->v_pool, h->H, h->T, h->D, h->pool_rows, row0,
+                                  (hipStream_t)stream) != 0)
+    return fail(KVC_ERR_HIP, "kv_cache_append_chunk: launch failed");
+  const int64_t id = h->table.next_chunk_id();
+  h->table.commit_append(slot);
+  if (out_chunk_id) *out_chunk_id = id;
+  if (out_slot) *out_slot = slot;
+  if (out_evicted) *out_evicted = evicted;
+  return KVC_OK;
+}
+
+int kv_cache_evict(kvc_handle h, int n, int64_t* out_ids, int* out_n) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "kv_cache_evict: handle is NULL");
+  if (n < 0) return fail(KVC_ERR_INVALID, "kv_cache_evict: n = %d < 0", n);
+  if (n > h->table.window_count())
+    return fail(KVC_ERR_STATE, "kv_cache_evict: %d requested, %d window chunks held", n,
+                h->table.window_count());
+  h->table.evict(n, out_ids);
+  if (out_n) *out_n = n;
+  return KVC_OK;
+}
+
+int kv_cache_reset(kvc_handle h) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "kv_cache_reset: handle is NULL");
+  h->table.reset();
+  return KVC_OK;
+}
+
+int kv_cache_query(kvc_handle h, int64_t* next_chunk_id, int* occupancy, int64_t* slot_chunk,
+                   int cap) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "kv_cache_query: handle is NULL");
+  if (next_chunk_id) *next_chunk_id = h->table.next_chunk_id();
+  if (occupancy) *occupancy = h->table.occupancy();
+  if (slot_chunk)
+    for (int s = 0; s < h->table.n_slots() && s < cap; ++s) slot_chunk[s] = h->table.slot_chunk(s);
+  return KVC_OK;
+}
+
+int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const void* v_cur,
+                          void* o, float* lse, float scale, void* stream) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "sink_window_attention: handle is NULL");
+  if (!q || !k_cur || !v_cur || !o)
+    return fail(KVC_ERR_INVALID, "sink_window_attention: NULL q, k_cur, v_cur or o");
+  if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)h->D);
+  if (!std::isfinite(scale)) return fail(KVC_ERR_INVALID, "sink_window_attention: scale not finite");
+  kvc::AttnArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = (const uint16_t*)q;
+  a.kcur = (const uint16_t*)k_cur;
+  a.vcur = (const uint16_t*)v_cur;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.kpool = (const uint16_t*)h->k_pool;
+  a.vpool = (const uint16_t*)h->v_pool;
+  a.pool_rows = h->pool_rows;
+  a.T = h->T;
+  a.H = h->H;
+  a.c = scale * 1.4426950408889634f;
+  const std::vector<kvc::Segment> segs = h->table.segments(h->T, h->Lc, true);
+  if ((int)segs.size() > kvc::kMaxSegments)
+    return fail(KVC_ERR_STATE, "sink_window_attention: %zu segments", segs.size());
+  a.nseg = (int)segs.size();
+  for (int i = 0; i < a.nseg; ++i) {
+    a.seg_row0[i] = segs[i].row0;
+    a.seg_len[i] = segs[i].len;
+  }
+  const int rc = kvc::launch_attention_bf16(a, h->D, h->variant, (hipStream_t)stream);
+  if (rc != 0) return fail(KVC_ERR_HIP, "sink_window_attention: launch failed");
+  return KVC_OK;
+}
+
+// ---- host-only slot table
+
+int kvc_table_create(int window_w, int n_sink, kvc_table_handle* out) {
+  g_last_error.clear();
+  if (!out) return fail(KVC_ERR_INVALID, "kvc_table_create: out is NULL");
+  if (window_w < 1 || n_sink < 0 || n_sink + window_w > KVC_MAX_SLOTS)
+    return fail(KVC_ERR_INVALID, "kvc_table_create: need W >= 1, n_sink >= 0, n_sink + W <= %d",
+                KVC_MAX_SLOTS);
+  kvc_table* t = new (std::nothrow) kvc_table(window_w, n_sink);
+  if (!t) return fail(KVC_ERR_OOM, "kvc_table_create: host allocation failed");
+  *out = t;
+  return KVC_OK;
+}
+
+int kvc_table_destroy(kvc_table_handle t) {
+  delete t;
+  return KVC_OK;
+}
+
+int kvc_table_append(kvc_table_handle t, int64_t* out_chunk_id, int* out_slot, int64_t* out_evicted) {
+  g_last_error.clear();
+  if (!t) return fail(KVC_ERR_INVALID, "kvc_table_append: handle is NULL");
+  int slot;
+  int64_t ev;
+  t->table.plan_append(&slot, &ev);
+  const int64_t id = t->table.next_chunk_id();
+  t->table.commit_append(slot);
+  if (out_chunk_id) *out_chunk_id = id;
+  if (out_slot) *out_slot = slot;
+  if (out_evicted) *out_evicted = ev;
+  return KVC_OK;
+}
+
+int kvc_table_evict(kvc_table_handle t, int n, int64_t* out_ids, int* out_n) {
+  g_last_error.clear();
+  if (!t) return fail(KVC_ERR_INVALID, "kvc_table_evict: handle is NULL");
+  if (n < 0) return fail(KVC_ERR_INVALID, "kvc_table_evict: n = %d < 0", n);
+  if (n > t->table.window_count())
+    return fail(KVC_ERR_STATE, "kvc_table_evict: %d requested, %d window chunks held", n,
+                t->table.window_count());
+  t->table.evict(n, out_ids);
+  if (out_n) *out_n = n;
+  return KVC_OK;
+}
+
+int kvc_table_reset(kvc_table_handle t) {
+  g_last_error.clear();
+  if (!t) return fail(KVC_ERR_INVALID, "kvc_table_reset: handle is NULL");
+  t->table.reset();
+  return KVC_OK;
+}
+
+int kvc_table_query(kvc_table_handle t, int64_t* next_chunk_id, int* occupancy, int64_t* slot_chunk,
+                    int cap) {
+  g_last_error.clear();
+  if (!t) return fail(KVC_ERR_INVALID, "kvc_table_query: handle is NULL");
+  if (next_chunk_id) *next_chunk_id = t->table.next_chunk_id();
+  if (occupancy) *occupancy = t->table.occupancy();
+  if (slot_chunk)
+    for (int s = 0; s < t->table.n_slots() && s < cap; ++s) slot_chunk[s] = t->table.slot_chunk(s);
+  return KVC_OK;
+}
+
+int kvc_table_segments(kvc_table_handle t, int chunk_tokens, int cond_len, int merge, int32_t* row0,
+                       int32_t* len, int cap, int* n_out) {
+  g_last_error.clear();
+  if (!t) return fail(KVC_ERR_INVALID, "kvc_table_segments: handle is NULL");
+  if (chunk_tokens < 1 || cond_len < 0)
+    return fail(KVC_ERR_INVALID, "kvc_table_segments: need T >= 1 and Lc >= 0");
+  const std::vector<kvc::Segment> segs = t->table.segments(chunk_tokens, cond_len, merge != 0);
+  if (n_out) *n_out = (int)segs.size();
+  if ((int)segs.size() > cap) return fail(KVC_ERR_INVALID, "kvc_table_segments: cap %d < %zu", cap, segs.size());
+  for (size_t i = 0; i < segs.size(); ++i) {
+    if (row0) row0[i] = segs[i].row0;
+    if (len) len[i] = segs[i].len;
+  }
+  return KVC_OK;
+}
+
+}  // extern "C"

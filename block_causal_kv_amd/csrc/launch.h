@@ -1,0 +1,39 @@
+// Kernel launch interfaces shared by the C-ABI layer and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+constexpr int kMaxSegments = 66;  // condition + up to 64 slots + spare
+
+// Arguments of one attention call.  Segments are pool row ranges of one head
+// (the same for every head); the current chunk is handled after them.
+struct AttnArgs {
+  const uint16_t* q;     // [H][T][D] bf16
+  const uint16_t* kcur;  // [H][T][D] bf16 (fp8: codes, see fp8 kernel)
+  const uint16_t* vcur;
+  uint16_t* o;           // [H][T][D] bf16
+  float* lse;            // [H][T] or null
+  const uint16_t* kpool; // [H][pool_rows][D]
+  const uint16_t* vpool;
+  int64_t pool_rows;
+  int T;
+  int H;
+  float c;  // softmax scale * log2(e)
+  int q_tiles;
+  int nseg;
+  int32_t seg_row0[kMaxSegments];
+  int32_t seg_len[kMaxSegments];
+};
+
+// variant: 0 = default tiling; others select alternative tilings (benchmarks).
+int launch_attention_bf16(AttnArgs& a, int head_dim, int variant, hipStream_t stream);
+
+// Copy src [H][rows][D] (bf16) into dst rows [row0, row0 + rows) of a pool
+// [H][pool_rows][D], for K and V in one launch.
+int launch_pool_write_bf16(const uint16_t* k_src, const uint16_t* v_src, uint16_t* k_pool,
+                           uint16_t* v_pool, int H, int rows, int D, int64_t pool_rows, int row0,
+                           hipStream_t stream);
+
+}  // namespace kvc

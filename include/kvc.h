@@ -1,0 +1,177 @@
+/*
+ * kvc.h - block-causal sink + sliding-window attention over a bounded KV cache
+ * for AMD MI355X (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * The method (JoyAI-Video-Edit; sources are named per entry point):
+ *   A video stream is cut into chunks of T latent tokens (time-aligned source
+ *   and target tokens).  The queries of the chunk being generated attend
+ *   bidirectionally to their own chunk, causally to the W most recent earlier
+ *   chunks, to the first chunk kept for good as a global sink, and to the
+ *   condition tokens.  After a chunk is generated its clean K/V are written to
+ *   a fixed-size cache, so memory and work per chunk stay level however long
+ *   the stream runs.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are DEVICE pointers, head-major [H][N][D] row-major (D fastest),
+ *     bfloat16 unless stated.  Chunk rows are source tokens then target tokens.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Device work is enqueued on it asynchronously, in call order.
+ *   - Return value: KVC_OK (0) or a negative KVC_ERR_* code.  On error nothing
+ *     is enqueued and the cache state is unchanged; kvc_last_error() gives a
+ *     message (thread-local).
+ *   - The host slot table is updated when a call returns, not when the stream
+ *     reaches it: issue the calls of one cache in order, on one stream, or
+ *     order the streams yourself.  A handle must not be used from two threads
+ *     at once.
+ *   - Ownership: the handle owns its device pool from create to destroy.  The
+ *     caller owns every buffer it passes, which must stay valid until the
+ *     stream has executed the call.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_OK 0
+#define KVC_ERR_INVALID (-1)     /* bad argument (shape, null pointer, range) */
+#define KVC_ERR_OOM (-2)         /* device allocation failed */
+#define KVC_ERR_HIP (-3)         /* a HIP runtime call failed */
+#define KVC_ERR_STATE (-4)       /* the call does not fit the cache's state */
+#define KVC_ERR_UNSUPPORTED (-5) /* valid but not implemented (e.g. head dim) */
+
+#define KVC_KV_BF16 0 /* cache holds bfloat16 K/V */
+#define KVC_KV_FP8 1  /* cache holds OCP e4m3 K/V codes + one float32 scale per (head, chunk) */
+
+#define KVC_MAX_SLOTS 64 /* n_sink + window */
+
+typedef struct kvc_cache* kvc_handle;
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* kvc_last_error(void);
+
+/*
+ * kv_cache_create - allocate a cache and its whole device pool, once.
+ *
+ * Source: tutorial (agifrontier.github.io), "From bidirectional editing to a
+ * chunk-wise causal architecture" (chunks, window of recent chunks, first chunk
+ * as a global sink) and "Hardware-software co-deployment", bullet "constant KV
+ * cache"; zhichai.net post, deployment paragraph (persistent memory pool).
+ *
+ *   chunk_tokens  T >= 1, tokens per chunk block (source + target)
+ *   window_w      W >= 1, earlier chunks kept besides the sink
+ *   n_sink        sink chunks (the pages: 1); n_sink + W <= KVC_MAX_SLOTS
+ *   cond_len      Lc >= 0, condition tokens
+ *   heads         H >= 1;  head_dim D in {64, 128}
+ *   kv_dtype      KVC_KV_BF16 or KVC_KV_FP8
+ *   out           receives the handle
+ * Pool: K and V each [H][Lc + (n_sink + W) * T][D] (bf16, or 1-byte codes),
+ * plus, for fp8, scales and a staging slot for the current chunk.  No device
+ * memory is allocated by any later call.  Errors: INVALID, UNSUPPORTED, OOM
+ * (nothing allocated, *out untouched), HIP.
+ */
+int kv_cache_create(int chunk_tokens, int window_w, int n_sink, int cond_len, int heads,
+                    int head_dim, int kv_dtype, kvc_handle* out);
+
+/* Free the pool and the handle (synchronises the device first).  NULL is a no-op. */
+int kv_cache_destroy(kvc_handle h);
+
+/*
+ * kv_cache_set_condition - write the condition tokens' K/V (each bf16
+ * [H][Lc][D]) into the pool's condition rows (quantised per head in fp8 mode).
+ * Source: neurohive.io review, "Architecture" (the MLLM emits condition tokens;
+ * figure caption: they are among the groups the active chunk attends to).
+ * Errors: INVALID (null pointer while Lc > 0), HIP.
+ */
+int kv_cache_set_condition(kvc_handle h, const void* k_cond, const void* v_cond, void* stream);
+
+/*
+ * kv_cache_append_chunk - write the clean K/V of the chunk just generated
+ * (each bf16 [H][T][D]) into its slot and update the slot table.
+ * Source: tutorial, "Hardware-software co-deployment", bullet "constant KV
+ * cache" (clean K/V are written to the cache right after generation).
+ * The chunk gets id next_chunk_id.  Chunks 0..n_sink-1 go to the sink slots;
+ * later chunks go round the W window slots, and when the target slot is
+ * occupied its chunk (the oldest window chunk) is evicted.
+ * Outputs (each may be NULL): chunk id, slot, evicted chunk id (-1 = none).
+ * fp8 mode: one float32 scale per (head, chunk) = amax / 448, codes rounded to
+ * nearest even and saturated.  Errors: INVALID, HIP.
+ */
+int kv_cache_append_chunk(kvc_handle h, const void* k, const void* v, void* stream,
+                          int64_t* out_chunk_id, int* out_slot, int64_t* out_evicted);
+
+/*
+ * kv_cache_evict - drop the n oldest window chunks (the sink is never evicted).
+ * Metadata only: no device work.  out_ids (may be NULL) receives the ids,
+ * oldest first; out_n (may be NULL) the count.
+ * Source: tutorial, "From bidirectional editing ..." (a fixed window of recent
+ * chunks); aiinking.com article, "Bounded KV cache".
+ * Errors: INVALID (n < 0), STATE (n > window chunks held; nothing evicted).
+ */
+int kv_cache_evict(kvc_handle h, int n, int64_t* out_ids, int* out_n);
+
+/* Drop every chunk, sink included, for a new stream; next chunk id is 0. */
+int kv_cache_reset(kvc_handle h);
+
+/*
+ * kv_cache_query - read the slot table.  Any output may be NULL.
+ *   next_chunk_id  id the next appended chunk gets (= the chunk attention computes)
+ *   occupancy      slots in use
+ *   slot_chunk     receives min(cap, n_sink + W) entries: chunk id per slot, -1 = empty
+ */
+int kv_cache_query(kvc_handle h, int64_t* next_chunk_id, int* occupancy, int64_t* slot_chunk,
+                   int cap);
+
+/*
+ * sink_window_attention - one attention call of the chunk being generated
+ * (id next_chunk_id, not yet in the cache).
+ * Source: tutorial, "From bidirectional editing to a chunk-wise causal
+ * architecture" (bidirectional inside the chunk, causal across chunks, window
+ * plus sink); neurohive.io review, "Chunks and fighting drift" and
+ * "Architecture" (figure caption: token groups visible to the active chunk).
+ *
+ *   q, k_cur, v_cur  bf16 [H][T][D]: the chunk's queries and its own K/V
+ *   o                bf16 [H][T][D] output
+ *   lse              float32 [H][T] or NULL: natural log of sum_j exp(scale * q.k_j)
+ *   scale            softmax scale; <= 0 selects 1/sqrt(D)
+ * For query i of head h: o_i = sum_j softmax_j(scale * q_i . k_j) v_j over the
+ * keys j of the condition tokens, every chunk resident in the cache, and the
+ * chunk's own T tokens.  fp8 mode: k_cur/v_cur are quantised like an append
+ * (per-head scale) before use.  Errors: INVALID, HIP.
+ */
+int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const void* v_cur,
+                          void* o, float* lse, float scale, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Host-only slot table: the same bookkeeping a cache handle owns, with no
+ * device memory.  Callable without a GPU; used to test the index logic.
+ * Same semantics and errors as the kv_cache_* calls of the same name.
+ */
+typedef struct kvc_table* kvc_table_handle;
+int kvc_table_create(int window_w, int n_sink, kvc_table_handle* out);
+int kvc_table_destroy(kvc_table_handle t);
+int kvc_table_append(kvc_table_handle t, int64_t* out_chunk_id, int* out_slot,
+                     int64_t* out_evicted);
+int kvc_table_evict(kvc_table_handle t, int n, int64_t* out_ids, int* out_n);
+int kvc_table_reset(kvc_table_handle t);
+int kvc_table_query(kvc_table_handle t, int64_t* next_chunk_id, int* occupancy,
+                    int64_t* slot_chunk, int cap);
+/*
+ * kvc_table_segments - the key segments (pool rows) a query of the next chunk
+ * reads from the pool: the condition rows [0, Lc) and each occupied slot s at
+ * rows [Lc + s*T, Lc + (s+1)*T); with merge != 0, physically adjacent runs are
+ * joined.  The chunk's own rows are not part of the pool and not listed.
+ * row0/len receive up to cap entries; *n_out the count (which may exceed cap:
+ * then INVALID).
+ */
+int kvc_table_segments(kvc_table_handle t, int chunk_tokens, int cond_len, int merge,
+                       int32_t* row0, int32_t* len, int cap, int* n_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

@@ -13,10 +13,10 @@ Recipe (stated once, used everywhere):
 * Streams are addressed by ``(seed, part)``: the condition tokens use part 0,
   chunk ``c`` uses part ``c + 1``.  Any chunk can therefore be regenerated on
   its own, without drawing the chunks before it.
-* Per chunk the draw order is: for each denoise step ``s`` the tensors
-  ``q_s, k_s, v_s``; then the clean ``k_clean, v_clean`` that are written to the
-  cache after the chunk is generated.  With ``clean_from_last_step=True`` no
-  clean tensors are drawn and the last step's K/V are used as the clean K/V.
+* Per chunk the draw order is: first the clean ``k_clean, v_clean`` that are
+  written to the cache after the chunk is generated, then for each denoise
+  step ``s`` the tensors ``q_s, k_s, v_s``.  With ``clean_from_last_step=True``
+  no clean tensors are drawn and the last step's K/V are the clean K/V.
 * Optional outliers: each (head, token) row of every K tensor is scaled by
   ``outlier_scale`` with probability ``outlier_frac`` (a Bernoulli drawn from the
   same generator right after the K tensor), before the bf16 rounding.
@@ -36,9 +36,10 @@ def to_bf16(x: np.ndarray) -> np.ndarray:
     Inputs here are finite normal draws, so no NaN handling is needed.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).reshape(x.shape)
+    u = x.view(np.uint32)
+    # finite inputs cannot carry past bit 31: the largest finite pattern is 0xFF7FFFFF
+    u = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) & np.uint32(0xFFFF0000)
+    return u.view(np.float32).reshape(x.shape)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -115,21 +116,28 @@ class ChunkInputs:
     v_clean: Optional[np.ndarray] = None
 
 
-def chunk_inputs(spec: StreamSpec, c: int, heads: Optional[int] = None) -> ChunkInputs:
-    """All inputs of chunk ``c`` (float32 arrays holding bf16 values)."""
+def chunk_inputs(spec: StreamSpec, c: int, heads: Optional[int] = None,
+                 clean_only: bool = False) -> ChunkInputs:
+    """Inputs of chunk ``c`` (float32 arrays holding bf16 values).
+
+    ``clean_only`` stops after the clean K/V (streams whose clean K/V are drawn
+    separately); the values drawn are the same as in a full call.
+    """
     h = spec.heads if heads is None else heads
     rng = np.random.default_rng((spec.seed, c + 1))
     shape = (h, spec.chunk_tokens, spec.head_dim)
     out = ChunkInputs()
+    if not spec.clean_from_last_step:
+        out.k_clean = _draw(rng, shape, True, spec)
+        out.v_clean = _draw(rng, shape, False, spec)
+        if clean_only:
+            return out
     for _ in range(spec.steps):
         out.q.append(_draw(rng, shape, False, spec))
         out.k.append(_draw(rng, shape, True, spec))
         out.v.append(_draw(rng, shape, False, spec))
     if spec.clean_from_last_step:
         out.k_clean, out.v_clean = out.k[-1], out.v[-1]
-    else:
-        out.k_clean = _draw(rng, shape, True, spec)
-        out.v_clean = _draw(rng, shape, False, spec)
     return out
 
 

@@ -1,0 +1,86 @@
+"""Helpers shared by the GPU tests: move seeded inputs to the device, run a
+stream through the C-ABI cache, and compare with the oracle."""
+from __future__ import annotations
+
+import sys
+from typing import Dict, Iterable, Optional
+
+import numpy as np
+
+import synthetic
+from oracle.cache import CacheModel
+from oracle.stream import attend_chunk
+
+BF16_MAX_ABS = 2e-2
+BF16_REL_L2 = 5e-3
+
+
+def to_dev(x: np.ndarray):
+    import torch
+    bits = synthetic.bf16_bits(x).view(np.int16)
+    return torch.from_numpy(bits).cuda().view(torch.bfloat16)
+
+
+def from_dev(t) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def errors(o: np.ndarray, ref: np.ndarray):
+    d = o - ref
+    return float(np.abs(d).max()), float(np.linalg.norm(d) / np.linalg.norm(ref))
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_stream(spec: synthetic.StreamSpec, check: Iterable[int], rows: Optional[np.ndarray] = None,
+               evict_plan: Optional[Dict[int, int]] = None, variant_env: Optional[str] = None,
+               max_abs: float = BF16_MAX_ABS, rel_l2: float = BF16_REL_L2, lse_tol: float = 1e-3):
+    """Run chunks 0..max(check) of ``spec``; compare attention at the chunks in
+    ``check`` (every step, the given rows or all) and every append's indices."""
+    import torch
+    from block_causal_kv_amd import KVCache
+
+    check = set(check)
+    H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
+    cache = KVCache(T, spec.window, spec.n_sink, spec.cond_len, H, D, spec.kv_dtype)
+    model = CacheModel(spec.window, spec.n_sink)
+    ck, cv = synthetic.cond_inputs(spec)
+    cache.set_condition(to_dev(ck), to_dev(cv))
+    clean_k, clean_v = {}, {}
+    worst = (0.0, 0.0)
+    for c in range(max(check) + 1):
+        if evict_plan and c in evict_plan:
+            n = evict_plan[c]
+            assert cache.evict(n) == model.evict(n)
+        need = c in check
+        x = synthetic.chunk_inputs(spec, c, clean_only=not need)
+        if need:
+            visible = model.resident() if evict_plan else None
+            for s in range(spec.steps):
+                say("  %s chunk %d step %d: attention H=%d T=%d D=%d" % (spec.name, c, s, H, T, D))
+                lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+                o = cache.attention(to_dev(x.q[s]), to_dev(x.k[s]), to_dev(x.v[s]), lse=lse)
+                torch.cuda.synchronize()
+                og, lg = from_dev(o), lse.cpu().numpy().astype(np.float64)
+                ref, ref_lse = attend_chunk(c, x.q[s], x.k[s], x.v[s], clean_k.__getitem__,
+                                            clean_v.__getitem__, ck, cv, spec.window, spec.n_sink,
+                                            spec.scale, rows=rows, visible=visible)
+                if rows is not None:
+                    og, lg = og[:, rows], lg[:, rows]
+                ma, rl = errors(og, ref)
+                le = float(np.abs(lg - ref_lse).max())
+                say("    max_abs %.3e rel_l2 %.3e lse_err %.3e" % (ma, rl, le))
+                assert np.isfinite(og).all()
+                assert ma <= max_abs and rl <= rel_l2, (c, s, ma, rl)
+                assert le <= lse_tol, (c, s, le)
+                worst = (max(worst[0], ma), max(worst[1], rl))
+        got = cache.append_chunk(to_dev(x.k_clean), to_dev(x.v_clean))
+        assert got == model.append(), (c, got)
+        assert cache.query()["slots"] == model.slot_map()
+        clean_k[c], clean_v[c] = x.k_clean, x.v_clean
+    torch.cuda.synchronize()
+    cache.close()
+    return worst
