@@ -162,9 +162,10 @@ def main() -> int:
         if ev is not None:
             ev[3].record(stream)
 
-    # fill the cache so every measured step is at steady state
+    # fill the cache (appends only) so every attention call below is at steady state
     for i in range(spec.n_sink + spec.window):
-        chunk_step(i)
+        s = sets[i % len(sets)]
+        cache.append_chunk(s["kc"], s["vc"], stream=stream)
     for i in range(args.warmup):
         chunk_step(i)
     torch.cuda.synchronize()
