@@ -42,6 +42,10 @@ struct kvc_cache {
   int64_t pool_rows;
   void* k_pool = nullptr;  // [H][pool_rows][D] bf16 (fp8: bytes)
   void* v_pool = nullptr;
+  int num_cus = 0;
+  float* ws_o = nullptr;   // attention workspace (partials of split query tiles)
+  float* ws_ml = nullptr;
+  int* ws_cnt = nullptr;
   kvc::SlotTable table;
   int variant = 0;  // attention tiling (0 = default)
   kvc_cache(int T_, int W_, int S_, int Lc_, int H_, int D_, int dt)
@@ -85,16 +89,32 @@ int kv_cache_create(int chunk_tokens, int window_w, int n_sink, int cond_len, in
     delete c;
     return hip_fail(e, "kv_cache_create: hipGetDevice");
   }
+  e = hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, c->device);
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(e, "kv_cache_create: hipDeviceGetAttribute");
+  }
   const size_t elem = 2;
   const size_t bytes = (size_t)heads * (size_t)pool_rows * (size_t)head_dim * elem;
+  const size_t n_cnt = (size_t)kvc::attention_max_units(chunk_tokens, heads);
   e = hipMalloc(&c->k_pool, bytes);
   if (e == hipSuccess) e = hipMalloc(&c->v_pool, bytes);
+  if (e == hipSuccess) e = hipMalloc(&c->ws_o, kvc::attention_ws_o_bytes(c->num_cus));
+  if (e == hipSuccess) e = hipMalloc(&c->ws_ml, kvc::attention_ws_ml_bytes(c->num_cus));
+  if (e == hipSuccess) e = hipMalloc(&c->ws_cnt, n_cnt * sizeof(int));
+  // the pool starts as zeros (finite values everywhere), the counters at zero
+  if (e == hipSuccess) e = hipMemset(c->k_pool, 0, bytes);
+  if (e == hipSuccess) e = hipMemset(c->v_pool, 0, bytes);
+  if (e == hipSuccess) e = hipMemset(c->ws_cnt, 0, n_cnt * sizeof(int));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
-    if (c->k_pool) (void)hipFree(c->k_pool);
+    for (void* p : {(void*)c->k_pool, (void*)c->v_pool, (void*)c->ws_o, (void*)c->ws_ml, (void*)c->ws_cnt})
+      if (p) (void)hipFree(p);
     (void)hipGetLastError();
     delete c;
     return fail(e == hipErrorOutOfMemory ? KVC_ERR_OOM : KVC_ERR_HIP,
-                "kv_cache_create: hipMalloc of 2 x %zu bytes failed: %s", bytes, hipGetErrorString(e));
+                "kv_cache_create: device allocation (pool 2 x %zu bytes + workspace) failed: %s", bytes,
+                hipGetErrorString(e));
   }
   if (const char* v = getenv("KVC_ATTN_VARIANT")) c->variant = atoi(v);
   *out = c;
@@ -107,8 +127,8 @@ int kv_cache_destroy(kvc_handle h) {
   int rc = KVC_OK;
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) rc = hip_fail(e, "kv_cache_destroy: hipDeviceSynchronize");
-  if (h->k_pool) (void)hipFree(h->k_pool);
-  if (h->v_pool) (void)hipFree(h->v_pool);
+  for (void* p : {(void*)h->k_pool, (void*)h->v_pool, (void*)h->ws_o, (void*)h->ws_ml, (void*)h->ws_cnt})
+    if (p) (void)hipFree(p);
   delete h;
   return rc;
 }
@@ -197,6 +217,10 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
   a.T = h->T;
   a.H = h->H;
   a.c = scale * 1.4426950408889634f;
+  a.num_cus = h->num_cus;
+  a.ws_o = h->ws_o;
+  a.ws_ml = h->ws_ml;
+  a.ws_cnt = h->ws_cnt;
   const std::vector<kvc::Segment> segs = h->table.segments(h->T, h->Lc, true);
   if ((int)segs.size() > kvc::kMaxSegments)
     return fail(KVC_ERR_STATE, "sink_window_attention: %zu segments", segs.size());

@@ -22,12 +22,30 @@ struct AttnArgs {
   int H;
   float c;  // softmax scale * log2(e)
   int q_tiles;
+  // persistent (stream-K) schedule: set by the launcher from num_cus
+  int num_cus;   // compute units of the device
+  int units;     // H * q_tiles
+  int tiles;     // key tiles per unit
+  int groups;    // persistent workgroups
+  int rounds;    // full rounds of whole units per workgroup
+  int rest;      // units left after the full rounds
+  int slices;    // key-range slices each rest unit is cut into
+  float* ws_o;   // partial O^T of sliced units: [num_cus][8 waves][16][64 lanes] float4
+  float* ws_ml;  // partial (max, sum): [num_cus][8][64] float2
+  int* ws_cnt;   // per-unit piece counters, zero between calls: [max units]
   int nseg;
   int32_t seg_row0[kMaxSegments];
   int32_t seg_len[kMaxSegments];
 };
 
-// variant: 0 = default tiling; others select alternative tilings (benchmarks).
+// Workspace of the persistent attention kernel, per cache: bytes of ws_o and ws_ml,
+// and the number of counters (units).
+size_t attention_ws_o_bytes(int num_cus);
+size_t attention_ws_ml_bytes(int num_cus);
+int attention_max_units(int T, int H);
+
+// variant: 0 = default (one workgroup per 128-row query tile, two per CU);
+// 2 = persistent ping-pong kernel with the rounds + slices schedule.
 int launch_attention_bf16(AttnArgs& a, int head_dim, int variant, hipStream_t stream);
 
 // Copy src [H][rows][D] (bf16) into dst rows [row0, row0 + rows) of a pool

@@ -60,3 +60,23 @@ def test_720p_sampled_rows():
     W = spec.window
     say("720p stream, sampled rows", len(rows))
     run_stream(spec, [0, 1, W, W + 1, W + 2, spec.n_chunks - 1], rows=rows)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid"])
+def test_persistent_kernel_variant(name, monkeypatch):
+    """The persistent ping-pong kernel (rounds of whole query tiles, then aligned
+    key-range slices merged by the last slice) against the oracle."""
+    monkeypatch.setenv("KVC_ATTN_VARIANT", "2")
+    spec = synthetic.SPECS[name]
+    say("persistent kernel,", name)
+    run_stream(spec, range(spec.n_chunks))
+
+
+def test_persistent_kernel_sliced_units(monkeypatch):
+    """A shape whose leftover query tiles are cut into key-range slices (H*ceil(T/256)
+    not a multiple of the CU count), with a ragged tail and two steps."""
+    monkeypatch.setenv("KVC_ATTN_VARIANT", "2")
+    spec = synthetic.small_spec("sliced", n_chunks=5, chunk_tokens=600, cond_len=40, heads=6, head_dim=128,
+                                window=2, steps=2, clean_from_last_step=False, outlier_frac=0.01, seed=17)
+    say("persistent kernel, sliced units", spec)
+    run_stream(spec, range(spec.n_chunks))
