@@ -113,7 +113,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="720p", choices=["720p", "mid", "long"])
+    ap.add_argument("--config", default="720p", choices=["720p", "mid", "long", "fp8"])
     ap.add_argument("--sets", type=int, default=4, help="distinct input sets cycled by step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -204,7 +204,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8 e4m3 K/V, fp8 MFMA" if spec.kv_dtype == "fp8" else "bf16",
         "data": "synthetic (seeded N(0,1), bf16; 1% of K rows x8)",
         "config": {"workload": workload_name(spec), "chunk_tokens": T, "cond_len": spec.cond_len,
                    "heads": H, "head_dim": D, "window": spec.window, "n_sink": spec.n_sink,

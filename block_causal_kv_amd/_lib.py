@@ -23,6 +23,8 @@ SIGNATURES = {
     "kv_cache_query": (C.c_int, [C.c_void_p, _I64P, _IP, _I64P, C.c_int]),
     "sink_window_attention": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                         C.c_void_p, C.c_float, C.c_void_p]),
+    "kv_cache_pool_view": (C.c_int, [C.c_void_p, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p),
+                                     C.POINTER(C.c_void_p), _I64P, _IP]),
     "kvc_table_create": (C.c_int, [C.c_int, C.c_int, C.POINTER(C.c_void_p)]),
     "kvc_table_destroy": (C.c_int, [C.c_void_p]),
     "kvc_table_append": (C.c_int, [C.c_void_p, _I64P, _IP, _I64P]),

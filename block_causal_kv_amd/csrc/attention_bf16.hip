@@ -44,106 +44,13 @@
 
 #include <type_traits>
 
+#include "attention_common.h"
 #include "launch.h"
 
 namespace kvc {
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
-typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
-
-constexpr float kNegInf = -__builtin_inff();
-constexpr int kBufFlags = 0x00020000;  // raw buffer resource, dword 3 (range-checked, no format)
-constexpr float kRescaleSlack = 8.0f;  // log2 units: accumulated exp2 values stay <= 256
-
-// max / sum of x over lanes l and l ^ 32, in every lane (v_permlane32_swap:
-// a VALU exchange between the two halves of the wave, no LDS round trip).
-__device__ __forceinline__ float max_halves(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
-}
-__device__ __forceinline__ float sum_halves(float x) {
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
-}
-
-// Two floats -> one dword of two bf16 (round to nearest even, v_cvt_pk_bf16_f32).
-// Operands are assembled from such dwords and bit-cast as whole vectors: with
-// this compiler, inserting or extracting single 16-bit elements of bf16 vectors
-// was seen to be compiled into repeated use of element 0.
-__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
-  const f32x2 v = {a, b};
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
-}
-
-__device__ __forceinline__ uint16_t f2bf(float x) {
-  __bf16 b = (__bf16)x;  // round to nearest even
-  return __builtin_bit_cast(uint16_t, b);
-}
-
-
-// Online-softmax step for one 32 x (32*KB) score tile held as S^T (one query
-// per lane, 16*KB keys per lane).  VALU results on gfx950 take ~20-36 cycles
-// to be usable, so the code is laid out as wide independent batches: a tree
-// for the row max, 32 independent fma then 32 independent exp2, and four
-// independent partial row sums.  Returns nothing; updates m_run, l_run, oacc
-// (rescaled only when the max grows by more than kRescaleSlack) and writes the
-// bf16 P^T operands.
-template <int KB, int DB>
-__device__ __forceinline__ void softmax_tile(f32x16 (&sacc)[KB], float& m_run, float& l_run,
-                                             f32x16 (&oacc)[DB], bf16x8 (&pb)[KB][2], float c) {
-  constexpr int NV = 16 * KB;
-  float v[NV];
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) v[kb * 16 + r] = sacc[kb][r];
-  // row max: pairwise tree (depth log2(NV))
-  float t[NV / 2];
-#pragma unroll
-  for (int i = 0; i < NV / 2; ++i) t[i] = fmaxf(v[2 * i], v[2 * i + 1]);
-#pragma unroll
-  for (int w = NV / 4; w >= 1; w /= 2)
-#pragma unroll
-    for (int i = 0; i < w; ++i) t[i] = fmaxf(t[i], t[i + w]);
-  const float mx = max_halves(t[0]) * c;
-  if (__any(mx > m_run + kRescaleSlack)) {
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-  }
-  const float nm = -m_run;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) v[i] = fmaf(v[i], c, nm);
-#pragma unroll
-  for (int i = 0; i < NV; ++i) v[i] = __builtin_amdgcn_exp2f(v[i]);
-  unsigned w[NV / 2];
-#pragma unroll
-  for (int i = 0; i < NV / 2; ++i) w[i] = pack_bf16(v[2 * i], v[2 * i + 1]);
-  float rs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < NV / 2; ++i)
-    rs[i & 3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[i]),
-                                                __builtin_bit_cast(bf16x2, 0x3f803f80u), rs[i & 3], false);
-  l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const u32x4 wv = {w[kb * 8 + h2 * 4 + 0], w[kb * 8 + h2 * 4 + 1], w[kb * 8 + h2 * 4 + 2], w[kb * 8 + h2 * 4 + 3]};
-      pb[kb][h2] = __builtin_bit_cast(bf16x8, wv);
-    }
-}
+using namespace dev;
 
 template <int D, int BN>
 struct Cfg {
@@ -166,38 +73,7 @@ struct Cfg {
 };
 
 // Segment cursor over [pool segments..., current chunk].
-// Segment cursor over [pool segments..., current chunk]; wave-uniform.  The
-// segment length is cached so the table is read only when a segment starts.
-struct Cursor {
-  int seg;
-  int off;
-  int len;
-};
-
-__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-// Scheduling pattern for a block of N LDS operand reads feeding N MFMAs: issue
-// 4 reads first, then alternate MFMA / read, so about 4 reads are in flight
-// while the MFMA pipe runs (one read ahead was not enough to hide LDS latency).
-template <int N>
-__device__ __forceinline__ void sched_reads_ahead() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-  for (int i = 0; i < N - 4; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-}
-
-// Feature flags of a kernel instance (tuning variants; the default is kDefaultFlags).
-constexpr int kFlagPermlane = 1;   // lane-half exchange by v_permlane32_swap (else ds_bpermute)
-constexpr int kFlagFastFetch = 2;  // unguarded loads for full tiles
-constexpr int kFlagSetprio = 4;    // raise wave priority while issuing MFMA blocks
-constexpr int kFlagBatched = 8;    // softmax laid out in wide independent batches
-constexpr int kDefaultFlags = kFlagPermlane;  // the unguarded fetch measured slower
-
-template <int D, int BN, int F>
+template <int D, int BN>
 __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
   using C = Cfg<D, BN>;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][C::K_LDS];
@@ -271,27 +147,16 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
     const int64_t base = seg_off(cur.seg) + (int64_t)cur.off * D;
     const uint16_t* kb = (cur.seg < a.nseg ? a.kpool : a.kcur) + base;
     const uint16_t* vb = (cur.seg < a.nseg ? a.vpool : a.vcur) + base;
-    if ((F & kFlagFastFetch) && valid == BN) {  // full tile (all but the last of a segment): no row checks
 #pragma unroll
-      for (int i = 0; i < C::KLOADS; ++i) {
-        const int idx = i * C::NT + tid;
-        kbuf[i] = *(const uint4*)(kb + (idx / C::CH) * D + (idx % C::CH) * 8);
-      }
-      if (v_job)
+    for (int i = 0; i < C::KLOADS; ++i) {
+      const int idx = i * C::NT + tid;
+      const int row = idx / C::CH, ch = idx % C::CH;
+      kbuf[i] = row < valid ? *(const uint4*)(kb + row * D + ch * 8) : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vbuf[i] = *(const uint4*)(vb + (4 * v_kq + i) * D + 8 * v_c8);
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::KLOADS; ++i) {
-        const int idx = i * C::NT + tid;
-        const int row = idx / C::CH, ch = idx % C::CH;
-        kbuf[i] = row < valid ? *(const uint4*)(kb + row * D + ch * 8) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 4 * v_kq + i;
-        vbuf[i] = (v_job && row < valid) ? *(const uint4*)(vb + row * D + 8 * v_c8) : make_uint4(0, 0, 0, 0);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * v_kq + i;
+      vbuf[i] = (v_job && row < valid) ? *(const uint4*)(vb + row * D + 8 * v_c8) : make_uint4(0, 0, 0, 0);
     }
   };
   auto stash = [&](int buf) {
@@ -341,7 +206,6 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
       const uint16_t* kl = k_lds[buf];
       const uint16_t* vl = v_lds[buf];
       // ---- S^T = K . Q^T
-      if (F & kFlagSetprio) __builtin_amdgcn_s_setprio(1);
       f32x16 sacc[C::KB];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
@@ -355,7 +219,6 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw), qreg[ds],
                                                               sacc[kb], 0, 0, 0);
         }
-      if (F & kFlagSetprio) __builtin_amdgcn_s_setprio(0);
       // ---- mask the tail of a partial tile: key of register r = kb*32 + 16*(r/8) + 8*hf + r%8
       if (valid < BN) {
 #pragma unroll
@@ -366,15 +229,12 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
       }
       // ---- online softmax
       bf16x8 pb[C::KB][2];  // P^T operands: [32-key block][16-key half]
-      if (F & kFlagBatched) {
-        softmax_tile<C::KB, C::DB>(sacc, m_run, l_run, oacc, pb, c);
-      } else {
       float mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = ((F & kFlagPermlane) ? max_halves(mx) : fmaxf(mx, __shfl_xor(mx, 32))) * c;
+      mx = max_halves(mx) * c;
       if (__any(mx > m_run + kRescaleSlack)) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -405,9 +265,7 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
           pb[kb][h2] = __builtin_bit_cast(bf16x8, wv);
         }
       l_run += rs;
-      }
       // ---- O^T += V^T . P^T
-      if (F & kFlagSetprio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < BN / 16; ++ks)
 #pragma unroll
@@ -416,7 +274,6 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw),
                                                               pb[ks >> 1][ks & 1], oacc[db], 0, 0, 0);
         }
-      if (F & kFlagSetprio) __builtin_amdgcn_s_setprio(0);
     }
     if (nxt.seg >= nseg_total) break;
     stash(buf ^ 1);  // buffer buf^1 was last read before the previous barrier
@@ -428,7 +285,7 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: O = O^T / l, bf16; lane holds dims db*32 + 8*(r/4) + 4*hf + r%4
-  const float l_tot = (F & kFlagPermlane) ? sum_halves(l_run) : l_run + __shfl_xor(l_run, 32);
+  const float l_tot = sum_halves(l_run);
   if (wave_active && qrow < T) {
     const float inv = 1.f / l_tot;
     uint16_t* dst = a.o + (head_rows + qrow) * D + 4 * hf;
@@ -823,13 +680,13 @@ int launch_sk(AttnArgs& a, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-template <int D, int BN, int F>
+template <int D, int BN>
 int launch_cfg(AttnArgs& a, hipStream_t stream) {
   using C = Cfg<D, BN>;
   a.q_tiles = (a.T + C::ROWS - 1) / C::ROWS;
   const int units = a.H * a.q_tiles;
   const int grid = 8 * ((units + 7) / 8);
-  hipLaunchKernelGGL((attention_bf16_kernel<D, BN, F>), dim3(grid), dim3(C::NT), 0, stream, a);
+  hipLaunchKernelGGL((attention_bf16_kernel<D, BN>), dim3(grid), dim3(C::NT), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -842,11 +699,11 @@ int attention_max_units(int T, int H) { return H * ((T + 255) / 256); }
 int launch_attention_bf16(AttnArgs& a, int head_dim, int variant, hipStream_t stream) {
   if (head_dim == 128) {
     if (variant == 2) return launch_sk<128, 64>(a, stream);
-    return launch_cfg<128, 64, kDefaultFlags>(a, stream);
+    return launch_cfg<128, 64>(a, stream);
   }
   if (head_dim == 64) {
     if (variant == 2) return launch_sk<64, 64>(a, stream);
-    return launch_cfg<64, 64, kDefaultFlags>(a, stream);
+    return launch_cfg<64, 64>(a, stream);
   }
   return -2;
 }

@@ -42,6 +42,12 @@ struct kvc_cache {
   int64_t pool_rows;
   void* k_pool = nullptr;  // [H][pool_rows][D] bf16 (fp8: bytes)
   void* v_pool = nullptr;
+  // fp8 cache: code pools with one spare slot for the current chunk, scales
+  int64_t rows8 = 0;       // Lc + (n_sink + W + 1) * T
+  size_t k8_bytes = 0, vt8_bytes = 0;
+  float* scales = nullptr;    // [2][H][blocks]: block 0 = condition, 1 + s = slot s, last = current
+  uint32_t* amax = nullptr;   // [2][H] scratch of the quantiser
+  int blocks() const { return n_sink + W + 2; }
   int num_cus = 0;
   float* ws_o = nullptr;   // attention workspace (partials of split query tiles)
   float* ws_ml = nullptr;
@@ -57,6 +63,17 @@ struct kvc_table {
   kvc::SlotTable table;
   kvc_table(int W, int S) : table(W, S) {}
 };
+
+namespace {
+
+// fp8 cache: quantise K/V bf16 [H][rows][D] into pool rows [row0, row0 + rows) with scale block blk.
+int quantize_into(kvc_cache* h, const void* k, const void* v, int rows, int row0, int blk, hipStream_t st) {
+  return kvc::launch_quantize_fp8((const uint16_t*)k, (const uint16_t*)v, h->H, rows, h->D, h->amax,
+                                  (uint8_t*)h->k_pool, h->rows8 * h->D, (uint8_t*)h->v_pool, h->rows8, row0,
+                                  h->scales + blk, h->H * h->blocks(), h->blocks(), st);
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -76,8 +93,12 @@ int kv_cache_create(int chunk_tokens, int window_w, int n_sink, int cond_len, in
                 KVC_MAX_SLOTS);
   if (head_dim != 64 && head_dim != 128)
     return fail(KVC_ERR_UNSUPPORTED, "kv_cache_create: head_dim %d not in {64, 128}", head_dim);
-  if (kv_dtype != KVC_KV_BF16)
+  if (kv_dtype != KVC_KV_BF16 && kv_dtype != KVC_KV_FP8)
     return fail(KVC_ERR_UNSUPPORTED, "kv_cache_create: kv_dtype %d not supported", kv_dtype);
+  if (kv_dtype == KVC_KV_FP8 && (chunk_tokens % 16 != 0 || cond_len % 16 != 0))
+    return fail(KVC_ERR_UNSUPPORTED,
+                "kv_cache_create: fp8 caches need T and Lc multiples of 16 (got T=%d Lc=%d)", chunk_tokens,
+                cond_len);
   const int64_t pool_rows = (int64_t)cond_len + (int64_t)(n_sink + window_w) * chunk_tokens;
   if (pool_rows > INT32_MAX || (int64_t)chunk_tokens * heads > INT32_MAX)
     return fail(KVC_ERR_INVALID, "kv_cache_create: sizes overflow 32-bit row indices");
@@ -94,11 +115,23 @@ int kv_cache_create(int chunk_tokens, int window_w, int n_sink, int cond_len, in
     delete c;
     return hip_fail(e, "kv_cache_create: hipDeviceGetAttribute");
   }
-  const size_t elem = 2;
-  const size_t bytes = (size_t)heads * (size_t)pool_rows * (size_t)head_dim * elem;
+  const bool fp8 = kv_dtype == KVC_KV_FP8;
+  c->rows8 = pool_rows + chunk_tokens;
+  const size_t elem = fp8 ? 1 : 2;
+  // fp8 pools hold one more slot (the current chunk) and 64 spare bytes
+  const size_t bytes = fp8 ? (size_t)heads * (size_t)c->rows8 * (size_t)head_dim + 64
+                           : (size_t)heads * (size_t)pool_rows * (size_t)head_dim * elem;
+  if (fp8 && bytes > (size_t)INT32_MAX) {
+    delete c;
+    return fail(KVC_ERR_INVALID, "kv_cache_create: fp8 code pool of %zu bytes exceeds 2^31", bytes);
+  }
+  c->k8_bytes = c->vt8_bytes = fp8 ? bytes : 0;
   const size_t n_cnt = (size_t)kvc::attention_max_units(chunk_tokens, heads);
   e = hipMalloc(&c->k_pool, bytes);
   if (e == hipSuccess) e = hipMalloc(&c->v_pool, bytes);
+  if (e == hipSuccess && fp8) e = hipMalloc(&c->scales, sizeof(float) * 2 * heads * c->blocks());
+  if (e == hipSuccess && fp8) e = hipMalloc(&c->amax, sizeof(uint32_t) * 2 * heads);
+  if (e == hipSuccess && fp8) e = hipMemset(c->scales, 0, sizeof(float) * 2 * heads * c->blocks());
   if (e == hipSuccess) e = hipMalloc(&c->ws_o, kvc::attention_ws_o_bytes(c->num_cus));
   if (e == hipSuccess) e = hipMalloc(&c->ws_ml, kvc::attention_ws_ml_bytes(c->num_cus));
   if (e == hipSuccess) e = hipMalloc(&c->ws_cnt, n_cnt * sizeof(int));
@@ -108,7 +141,8 @@ int kv_cache_create(int chunk_tokens, int window_w, int n_sink, int cond_len, in
   if (e == hipSuccess) e = hipMemset(c->ws_cnt, 0, n_cnt * sizeof(int));
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
-    for (void* p : {(void*)c->k_pool, (void*)c->v_pool, (void*)c->ws_o, (void*)c->ws_ml, (void*)c->ws_cnt})
+    for (void* p : {(void*)c->k_pool, (void*)c->v_pool, (void*)c->ws_o, (void*)c->ws_ml, (void*)c->ws_cnt,
+                    (void*)c->scales, (void*)c->amax})
       if (p) (void)hipFree(p);
     (void)hipGetLastError();
     delete c;
@@ -127,7 +161,8 @@ int kv_cache_destroy(kvc_handle h) {
   int rc = KVC_OK;
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) rc = hip_fail(e, "kv_cache_destroy: hipDeviceSynchronize");
-  for (void* p : {(void*)h->k_pool, (void*)h->v_pool, (void*)h->ws_o, (void*)h->ws_ml, (void*)h->ws_cnt})
+  for (void* p : {(void*)h->k_pool, (void*)h->v_pool, (void*)h->ws_o, (void*)h->ws_ml, (void*)h->ws_cnt,
+                  (void*)h->scales, (void*)h->amax})
     if (p) (void)hipFree(p);
   delete h;
   return rc;
@@ -138,6 +173,11 @@ int kv_cache_set_condition(kvc_handle h, const void* k_cond, const void* v_cond,
   if (!h) return fail(KVC_ERR_INVALID, "kv_cache_set_condition: handle is NULL");
   if (h->Lc == 0) return KVC_OK;
   if (!k_cond || !v_cond) return fail(KVC_ERR_INVALID, "kv_cache_set_condition: NULL K or V");
+  if (h->kv_dtype == KVC_KV_FP8) {
+    if (quantize_into(h, k_cond, v_cond, h->Lc, 0, 0, (hipStream_t)stream) != 0)
+      return fail(KVC_ERR_HIP, "kv_cache_set_condition: launch failed");
+    return KVC_OK;
+  }
   if (kvc::launch_pool_write_bf16((const uint16_t*)k_cond, (const uint16_t*)v_cond,
                                   (uint16_t*)h->k_pool, (uint16_t*)h->v_pool, h->H, h->Lc, h->D,
                                   h->pool_rows, 0, (hipStream_t)stream) != 0)
@@ -154,10 +194,12 @@ int kv_cache_append_chunk(kvc_handle h, const void* k, const void* v, void* stre
   int64_t evicted;
   h->table.plan_append(&slot, &evicted);
   const int row0 = h->Lc + slot * h->T;
-  if (kvc::launch_pool_write_bf16((const uint16_t*)k, (const uint16_t*)v, (uint16_t*)h->k_pool,
-                                  (uint16_t*)h->v_pool, h->H, h->T, h->D, h->pool_rows, row0,
-                                  (hipStream_t)stream) != 0)
-    return fail(KVC_ERR_HIP, "kv_cache_append_chunk: launch failed");
+  const int rc = h->kv_dtype == KVC_KV_FP8
+                     ? quantize_into(h, k, v, h->T, row0, 1 + slot, (hipStream_t)stream)
+                     : kvc::launch_pool_write_bf16((const uint16_t*)k, (const uint16_t*)v, (uint16_t*)h->k_pool,
+                                                   (uint16_t*)h->v_pool, h->H, h->T, h->D, h->pool_rows, row0,
+                                                   (hipStream_t)stream);
+  if (rc != 0) return fail(KVC_ERR_HIP, "kv_cache_append_chunk: launch failed");
   const int64_t id = h->table.next_chunk_id();
   h->table.commit_append(slot);
   if (out_chunk_id) *out_chunk_id = id;
@@ -221,6 +263,39 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
   a.ws_o = h->ws_o;
   a.ws_ml = h->ws_ml;
   a.ws_cnt = h->ws_cnt;
+  if (h->kv_dtype == KVC_KV_FP8) {
+    // every chunk has its own scales: one segment per block, the current chunk
+    // quantised into the spare slot after the window slots
+    const std::vector<kvc::Segment> segs = h->table.segments(h->T, h->Lc, false);
+    if ((int)segs.size() + 1 > kvc::kMaxSegments)
+      return fail(KVC_ERR_STATE, "sink_window_attention: %zu segments", segs.size());
+    const int n_slots = h->n_sink + h->W;
+    const int cur_row0 = h->Lc + n_slots * h->T;
+    a.nseg = 0;
+    for (const kvc::Segment& sg : segs) {
+      a.seg_row0[a.nseg] = sg.row0;
+      a.seg_len[a.nseg] = sg.len;
+      a.seg_blk[a.nseg] = sg.row0 < h->Lc ? 0 : 1 + (sg.row0 - h->Lc) / h->T;
+      ++a.nseg;
+    }
+    a.seg_row0[a.nseg] = cur_row0;
+    a.seg_len[a.nseg] = h->T;
+    a.seg_blk[a.nseg] = n_slots + 1;
+    ++a.nseg;
+    a.k8 = (const uint8_t*)h->k_pool;
+    a.vt8 = (const uint8_t*)h->v_pool;
+    a.k8_bytes = (int64_t)h->k8_bytes;
+    a.vt8_bytes = (int64_t)h->vt8_bytes;
+    a.pool_rows8 = h->rows8;
+    a.scales = h->scales;
+    a.scale_tensor = h->H * h->blocks();
+    a.scale_head = h->blocks();
+    if (quantize_into(h, k_cur, v_cur, h->T, cur_row0, n_slots + 1, (hipStream_t)stream) != 0)
+      return fail(KVC_ERR_HIP, "sink_window_attention: quantise launch failed");
+    if (kvc::launch_attention_fp8(a, h->D, (hipStream_t)stream) != 0)
+      return fail(KVC_ERR_HIP, "sink_window_attention: launch failed");
+    return KVC_OK;
+  }
   const std::vector<kvc::Segment> segs = h->table.segments(h->T, h->Lc, true);
   if ((int)segs.size() > kvc::kMaxSegments)
     return fail(KVC_ERR_STATE, "sink_window_attention: %zu segments", segs.size());
@@ -231,6 +306,18 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
   }
   const int rc = kvc::launch_attention_bf16(a, h->D, h->variant, (hipStream_t)stream);
   if (rc != 0) return fail(KVC_ERR_HIP, "sink_window_attention: launch failed");
+  return KVC_OK;
+}
+
+int kv_cache_pool_view(kvc_handle h, const void** k_pool, const void** v_pool, const float** scales,
+                       int64_t* rows, int* blocks) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "kv_cache_pool_view: handle is NULL");
+  if (k_pool) *k_pool = h->k_pool;
+  if (v_pool) *v_pool = h->v_pool;
+  if (scales) *scales = h->scales;
+  if (rows) *rows = h->kv_dtype == KVC_KV_FP8 ? h->rows8 : h->pool_rows;
+  if (blocks) *blocks = h->kv_dtype == KVC_KV_FP8 ? h->blocks() : 0;
   return KVC_OK;
 }
 

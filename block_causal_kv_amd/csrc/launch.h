@@ -36,6 +36,17 @@ struct AttnArgs {
   int nseg;
   int32_t seg_row0[kMaxSegments];
   int32_t seg_len[kMaxSegments];
+  // fp8 cache (kv_dtype fp8): every segment, the current chunk included, lives
+  // in the code pools; seg_blk is the segment's scale block.
+  const uint8_t* k8;     // K codes [H][pool_rows8][D]
+  const uint8_t* vt8;    // V codes, transposed: [H][D][pool_rows8]
+  int64_t k8_bytes;      // allocation sizes (range of the buffer loads)
+  int64_t vt8_bytes;
+  int64_t pool_rows8;
+  const float* scales;   // [2 (K, V)][H][blocks]
+  int scale_tensor;      // H * blocks
+  int scale_head;        // blocks
+  int32_t seg_blk[kMaxSegments];
 };
 
 // Workspace of the persistent attention kernel, per cache: bytes of ws_o and ws_ml,
@@ -53,5 +64,16 @@ int launch_attention_bf16(AttnArgs& a, int head_dim, int variant, hipStream_t st
 int launch_pool_write_bf16(const uint16_t* k_src, const uint16_t* v_src, uint16_t* k_pool,
                            uint16_t* v_pool, int H, int rows, int D, int64_t pool_rows, int row0,
                            hipStream_t stream);
+
+// fp8 attention (E4M3 K/V codes, per-(head, chunk) scales).
+int launch_attention_fp8(AttnArgs& a, int head_dim, hipStream_t stream);
+
+// Quantise K and V (bf16 [H][rows][D]) into E4M3 codes: K row-major into
+// k_dst[h*k_head + (row0 + r)*D + d], V transposed into vt_dst[(h*D + d)*vt_rows + row0 + r];
+// scales[t*scale_tensor + h*scale_head] <- amax/448 (t = 0 K, 1 V).  amax_bits:
+// 2*H words of scratch.
+int launch_quantize_fp8(const uint16_t* k, const uint16_t* v, int H, int rows, int D, uint32_t* amax_bits,
+                        uint8_t* k_dst, int64_t k_head, uint8_t* vt_dst, int64_t vt_rows, int row0,
+                        float* scales, int scale_tensor, int scale_head, hipStream_t stream);
 
 }  // namespace kvc

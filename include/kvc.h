@@ -66,7 +66,7 @@ const char* kvc_last_error(void);
  *   n_sink        sink chunks (the pages: 1); n_sink + W <= KVC_MAX_SLOTS
  *   cond_len      Lc >= 0, condition tokens
  *   heads         H >= 1;  head_dim D in {64, 128}
- *   kv_dtype      KVC_KV_BF16 or KVC_KV_FP8
+ *   kv_dtype      KVC_KV_BF16 or KVC_KV_FP8 (fp8 needs T and Lc multiples of 16)
  *   out           receives the handle
  * Pool: K and V each [H][Lc + (n_sink + W) * T][D] (bf16, or 1-byte codes),
  * plus, for fp8, scales and a staging slot for the current chunk.  No device
@@ -144,6 +144,21 @@ int kv_cache_query(kvc_handle h, int64_t* next_chunk_id, int* occupancy, int64_t
  */
 int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const void* v_cur,
                           void* o, float* lse, float scale, void* stream);
+
+/*
+ * kv_cache_pool_view - device addresses of the pool, for inspection (tests,
+ * tools).  Read-only use; valid until destroy.  Any output may be NULL.
+ *   k_pool   bf16: K [H][rows][D].  fp8: K codes [H][rows][D] (1 byte each)
+ *   v_pool   bf16: V [H][rows][D].  fp8: V codes transposed, [H][D][rows]
+ *   scales   fp8: float32 [2 (K, V)][H][blocks]; block 0 = condition rows,
+ *            1 + s = slot s, blocks - 1 = the current chunk of the last
+ *            attention call.  NULL for bf16.
+ *   rows     pool rows: Lc + (n_sink + W) * T (bf16) or Lc + (n_sink + W + 1) * T
+ *            (fp8: one more slot for the current chunk); slot s starts at Lc + s*T
+ *   blocks   fp8: n_sink + W + 2; bf16: 0
+ */
+int kv_cache_pool_view(kvc_handle h, const void** k_pool, const void** v_pool, const float** scales,
+                       int64_t* rows, int* blocks);
 
 /* ---------------------------------------------------------------------------
  * Host-only slot table: the same bookkeeping a cache handle owns, with no
