@@ -108,6 +108,71 @@ def cpu_baseline(spec: synthetic.StreamSpec, budget_s: float = 12.0) -> dict:
                                            spec.steps * flop_per_call(spec) / (flop / dt) * 1e3)}
 
 
+def flatness_stats(ms, first_steady: int) -> dict:
+    """Flatness of per-chunk latency over the steady chunks (those whose cache
+    holds the sink and a full window): p99/p50, least-squares slope over the
+    stream, and the slope times the stream length relative to the median."""
+    y = np.asarray(ms[first_steady:], dtype=np.float64)
+    x = np.arange(first_steady, first_steady + y.size, dtype=np.float64)
+    slope = float(np.polyfit(x, y, 1)[0])
+    p50 = float(np.percentile(y, 50))
+    return {"steady_chunks": int(y.size), "p50_ms": round(p50, 4),
+            "p99_ms": round(float(np.percentile(y, 99)), 4), "max_ms": round(float(y.max()), 4),
+            "p99_over_p50": round(float(np.percentile(y, 99)) / p50, 4),
+            "slope_ms_per_chunk": slope, "drift_over_stream_frac": abs(slope) * len(ms) / p50}
+
+
+def flatness(args) -> int:
+    """300-chunk long stream from an empty cache: per-chunk-step latency (two
+    attention calls + append, HIP events) and device memory before and after."""
+    import torch
+    from block_causal_kv_amd import KVCache
+
+    spec = synthetic.SPECS["long"]
+    H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
+    dev = torch.device("cuda", 0)
+
+    def dev_bf16(x):
+        return torch.from_numpy(synthetic.bf16_bits(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    ck, cv = synthetic.cond_inputs(spec)
+    sets = []
+    for i in range(args.sets):  # chunk c uses input set c % sets
+        x = synthetic.chunk_inputs(spec, i)
+        sets.append(([dev_bf16(a) for a in x.q], [dev_bf16(a) for a in x.k], [dev_bf16(a) for a in x.v],
+                     dev_bf16(x.k_clean), dev_bf16(x.v_clean)))
+    out = torch.empty((H, T, D), dtype=torch.bfloat16, device=dev)
+    cache = KVCache(T, spec.window, spec.n_sink, spec.cond_len, H, D, spec.kv_dtype)
+    cache.set_condition(dev_bf16(ck), dev_bf16(cv))
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0] + torch.cuda.memory_reserved()  # memory outside torch's pool
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(spec.n_chunks)]
+    for c in range(spec.n_chunks):
+        q, k, v, kc, vc = sets[c % len(sets)]
+        ev[c][0].record(stream)
+        for st in range(spec.steps):
+            cache.attention(q[st], k[st], v[st], out=out, stream=stream)
+        cache.append_chunk(kc, vc, stream=stream)
+        ev[c][1].record(stream)
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0] + torch.cuda.memory_reserved()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    first_steady = spec.n_sink + spec.window + 1
+    st = flatness_stats(ms, first_steady)
+    rec = {"metric": "per-chunk-step latency flatness over a 300-chunk stream", "value": st["p99_over_p50"],
+           "unit": "p99/p50", "higher_is_better": False, "n_gpus": 1, "data": "synthetic",
+           "dtype": "bf16", "config": {"workload": workload_name(spec), "chunks": spec.n_chunks,
+                                       "input_sets": len(sets)},
+           "flatness": st, "device_bytes_allocated_during_stream": int(free0 - free1),
+           "ms_first_chunks": [round(m, 3) for m in ms[:first_steady + 1]],
+           "ms_per_chunk_step_mean_steady": round(float(np.mean(ms[first_steady:])), 4)}
+    cache.close()
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +181,9 @@ def main() -> int:
     ap.add_argument("--config", default="720p", choices=["720p", "mid", "long", "fp8"])
     ap.add_argument("--sets", type=int, default=4, help="distinct input sets cycled by step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flatness", action="store_true",
+                    help="stream the 300-chunk long config from an empty cache and report per-chunk "
+                         "latency flatness and device memory instead of the throughput line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: attention shards by heads with no exchange, so "
@@ -127,6 +195,8 @@ def main() -> int:
     from block_causal_kv_amd import KVCache
     sys.path.insert(0, os.path.join(ROOT, "tests"))
 
+    if args.flatness:
+        return flatness(args)
     spec = synthetic.SPECS[args.config]
     H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
     dev = torch.device("cuda", 0)

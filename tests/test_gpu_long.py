@@ -1,0 +1,78 @@
+"""The 300-chunk long stream (720p sizes, H = 32, W = 8 + sink): cache indices
+bit-exact for every append, outputs against the oracle at spot chunks, flat
+per-chunk latency and no device allocation after create.  Inputs cycle through
+a few seeded sets (chunk c uses set c % 4); the oracle sees the same arrays."""
+import numpy as np
+import pytest
+
+import synthetic
+from oracle.cache import CacheModel
+from oracle.stream import attend_chunk
+from streams import BF16_MAX_ABS, BF16_REL_L2, errors, from_dev, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SETS = 4
+
+
+@pytest.mark.timeout(1200)
+def test_long_stream_indices_outputs_flatness_memory():
+    import torch
+    from block_causal_kv_amd import KVCache
+    spec = synthetic.SPECS["long"]
+    H, T, D, W, S = spec.heads, spec.chunk_tokens, spec.head_dim, spec.window, spec.n_sink
+    say("long stream", spec)
+    ck, cv = synthetic.cond_inputs(spec)
+    host = [synthetic.chunk_inputs(spec, i) for i in range(SETS)]
+    dev = [([to_dev(a) for a in x.q], [to_dev(a) for a in x.k], [to_dev(a) for a in x.v],
+            to_dev(x.k_clean), to_dev(x.v_clean)) for x in host]
+    cache = KVCache(T, W, S, spec.cond_len, H, D)
+    cache.set_condition(to_dev(ck), to_dev(cv))
+    model = CacheModel(W, S)
+    out = torch.empty((H, T, D), dtype=torch.bfloat16, device="cuda")
+    spot = {0: None, W + 1: None, 150: None, spec.n_chunks - 1: None}
+    heads = [0, H - 1]
+    rows = np.array(sorted(set(range(0, T, 251)) | set(range(T - 8, T))))
+    # Device memory not held by torch's caching allocator, from chunk WARM on
+    # (runtime pools at their steady size; the loop synchronises every chunk):
+    # any allocation by the library during the stream would lower it.
+    WARM = 20
+    free0 = None
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(spec.n_chunks)]
+    for c in range(spec.n_chunks):
+        q, k, v, kc, vc = dev[c % SETS]
+        ev[c][0].record()
+        for st in range(spec.steps):
+            cache.attention(q[st], k[st], v[st], out=out)
+        got = cache.append_chunk(kc, vc)
+        ev[c][1].record()
+        if c in spot:  # the last step's output (the append does not touch it)
+            spot[c] = from_dev(out)[heads][:, rows]
+        torch.cuda.synchronize()
+        if c == WARM:
+            free0 = torch.cuda.mem_get_info()[0] + torch.cuda.memory_reserved()
+        assert got == model.append(), (c, got)
+        assert cache.query()["slots"] == model.slot_map(), c
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0] + torch.cuda.memory_reserved()
+    assert free0 == free1, "device memory changed during the stream"
+    # outputs at the spot chunks (last denoise step), heads 0 and H-1, sampled rows
+    cyc = lambda attr: (lambda j: getattr(host[j % SETS], attr))
+    for c, got in spot.items():
+        x = host[c % SETS]
+        say("  oracle at chunk", c)
+        ref, _ = attend_chunk(c, x.q[-1], x.k[-1], x.v[-1], cyc("k_clean"), cyc("v_clean"), ck, cv, W, S,
+                              spec.scale, rows=rows, heads=heads)
+        ma, rl = errors(got, ref)
+        say("    max_abs %.3e rel_l2 %.3e" % (ma, rl))
+        assert ma <= BF16_MAX_ABS and rl <= BF16_REL_L2, (c, ma, rl)
+    # flatness over the steady chunks (cache holds the sink and a full window)
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    y = ms[S + W + 1:]
+    p50 = np.percentile(y, 50)
+    slope = np.polyfit(np.arange(y.size), y, 1)[0]
+    say("  per-chunk ms: p50 %.4f p99 %.4f max %.4f slope %.3e" % (p50, np.percentile(y, 99), y.max(), slope))
+    # generous bounds: catch growth with stream length, not clock noise
+    assert np.percentile(y, 99) / p50 <= 1.25
+    assert abs(slope) * spec.n_chunks <= 0.05 * p50
+    cache.close()
