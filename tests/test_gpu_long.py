@@ -72,7 +72,12 @@ def test_long_stream_indices_outputs_flatness_memory():
     p50 = np.percentile(y, 50)
     slope = np.polyfit(np.arange(y.size), y, 1)[0]
     say("  per-chunk ms: p50 %.4f p99 %.4f max %.4f slope %.3e" % (p50, np.percentile(y, 99), y.max(), slope))
-    # generous bounds: catch growth with stream length, not clock noise
+    # The claim is that cost does not grow with stream length: bound the growth
+    # (one-sided; a fresh device's clocks may still be settling and make early
+    # chunks slower) and the spread, generously enough to ignore clock noise.
     assert np.percentile(y, 99) / p50 <= 1.25
-    assert abs(slope) * spec.n_chunks <= 0.05 * p50
+    assert slope * spec.n_chunks <= 0.05 * p50
+    late, early = np.median(y[-50:]), np.median(y[:50])
+    say("  median of first / last 50 steady chunks: %.4f / %.4f" % (early, late))
+    assert late <= 1.05 * early
     cache.close()
