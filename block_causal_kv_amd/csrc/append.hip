@@ -1,11 +1,14 @@
-// Ring-buffer append of clean K/V into the bounded cache (bf16).
+// Cache writes of bf16 K/V: the ring-buffer append of a clean chunk, the
+// condition rows, and the current chunk's V before an attention call.
 //
 // After a chunk is generated its clean K/V are written into the cache slot the
 // host slot table picked (JoyAI-Video-Edit tutorial, agifrontier.github.io,
-// section "Hardware-software co-deployment", bullet "constant KV cache").  The
-// same kernel writes the condition rows.  The copy is HBM-bound: each thread
-// moves 16-byte vectors, consecutive threads touch consecutive addresses, and
-// K and V go in one launch (blockIdx.y).
+// section "Hardware-software co-deployment", bullet "constant KV cache").
+// K is stored row-major like the input, so its write is a plain copy: each
+// thread moves 16-byte vectors and consecutive threads touch consecutive
+// addresses.  V is stored transposed ([D][rows] per head), the layout the PV
+// product reads its MFMA operand in; the transpose goes through an LDS tile so
+// both the reads and the writes are 16-byte and coalesced.
 #include <hip/hip_runtime.h>
 
 #include "launch.h"
@@ -13,14 +16,9 @@
 namespace kvc {
 namespace {
 
-__global__ __launch_bounds__(256) void pool_write_bf16_kernel(const uint4* __restrict__ k_src,
-                                                              const uint4* __restrict__ v_src,
-                                                              uint4* __restrict__ k_pool,
-                                                              uint4* __restrict__ v_pool,
-                                                              int64_t vecs_per_head, int64_t pool_head_vecs,
-                                                              int64_t row0_vecs, int64_t total) {
-  const uint4* src = blockIdx.y == 0 ? k_src : v_src;
-  uint4* dst = blockIdx.y == 0 ? k_pool : v_pool;
+__global__ __launch_bounds__(256) void rows_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                        int64_t vecs_per_head, int64_t pool_head_vecs,
+                                                        int64_t row0_vecs, int64_t total) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t h = i / vecs_per_head;
@@ -29,20 +27,66 @@ __global__ __launch_bounds__(256) void pool_write_bf16_kernel(const uint4* __res
   }
 }
 
+// One block: 64 rows of one head (grid: row tiles x H).  Rows past `rows` read
+// as zero, so the last 8-column piece is completed with zeros.
+template <int D>
+__global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t* __restrict__ src,
+                                                          uint16_t* __restrict__ vt, int rows, int64_t vt_rows,
+                                                          int col0) {
+  constexpr int TR = 64;
+  constexpr int STR = TR + 8;  // LDS row stride (elements) of the transposed tile
+  __shared__ __attribute__((aligned(16))) uint16_t tile[D * STR];
+  const int h = blockIdx.y;
+  const int r0 = blockIdx.x * TR;
+  const uint16_t* s = src + ((int64_t)h * rows + r0) * D;
+  constexpr int CH = D / 8;  // 16-byte pieces per input row
+  for (int idx = threadIdx.x; idx < TR * CH; idx += blockDim.x) {
+    const int r = idx / CH, c8 = idx % CH;
+    const uint4 w = r0 + r < rows ? *(const uint4*)(s + (int64_t)r * D + c8 * 8) : make_uint4(0, 0, 0, 0);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tile[(c8 * 8 + 2 * j) * STR + r] = (uint16_t)(ws[j] & 0xFFFFu);
+      tile[(c8 * 8 + 2 * j + 1) * STR + r] = (uint16_t)(ws[j] >> 16);
+    }
+  }
+  __syncthreads();
+  const int nr = min(TR, rows - r0);
+  const int npieces = (nr + 7) / 8;  // 8-column pieces holding at least one row
+  for (int idx = threadIdx.x; idx < D * (TR / 8); idx += blockDim.x) {
+    const int d = idx / (TR / 8), p = idx % (TR / 8);
+    if (p >= npieces) continue;
+    const uint4 w = *(const uint4*)(&tile[d * STR + 8 * p]);
+    *(uint4*)(vt + ((int64_t)h * D + d) * vt_rows + col0 + r0 + 8 * p) = w;
+  }
+}
+
 }  // namespace
 
-int launch_pool_write_bf16(const uint16_t* k_src, const uint16_t* v_src, uint16_t* k_pool,
-                           uint16_t* v_pool, int H, int rows, int D, int64_t pool_rows, int row0,
-                           hipStream_t stream) {
+int launch_rows_copy_bf16(const uint16_t* src, uint16_t* pool, int H, int rows, int D, int64_t pool_rows,
+                          int row0, hipStream_t stream) {
   const int64_t vec_per_row = D / 8;
   const int64_t vecs_per_head = (int64_t)rows * vec_per_row;
   const int64_t total = (int64_t)H * vecs_per_head;
   if (total == 0) return 0;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(pool_write_bf16_kernel, dim3((unsigned)blocks, 2), dim3(256), 0, stream,
-                     (const uint4*)k_src, (const uint4*)v_src, (uint4*)k_pool, (uint4*)v_pool,
-                     vecs_per_head, pool_rows * vec_per_row, (int64_t)row0 * vec_per_row, total);
+  hipLaunchKernelGGL(rows_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (const uint4*)src,
+                     (uint4*)pool, vecs_per_head, pool_rows * vec_per_row, (int64_t)row0 * vec_per_row, total);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_transpose_v_bf16(const uint16_t* src, uint16_t* vt, int H, int rows, int D, int64_t vt_rows,
+                            int col0, hipStream_t stream) {
+  if (rows <= 0) return 0;
+  if ((col0 & 7) != 0 || (vt_rows & 7) != 0) return -2;
+  const dim3 grid((rows + 63) / 64, H);
+  if (D == 128)
+    hipLaunchKernelGGL(transpose_v_kernel<128>, grid, dim3(256), 0, stream, src, vt, rows, vt_rows, col0);
+  else if (D == 64)
+    hipLaunchKernelGGL(transpose_v_kernel<64>, grid, dim3(256), 0, stream, src, vt, rows, vt_rows, col0);
+  else
+    return -2;
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -39,24 +39,22 @@ int hip_fail(hipError_t e, const char* what) {
 struct kvc_cache {
   int T, W, n_sink, Lc, H, D, kv_dtype;
   int device;
-  int64_t pool_rows;
-  void* k_pool = nullptr;  // [H][pool_rows][D] bf16 (fp8: bytes)
-  void* v_pool = nullptr;
-  // fp8 cache: code pools with one spare slot for the current chunk, scales
-  int64_t rows8 = 0;       // Lc + (n_sink + W + 1) * T
-  size_t k8_bytes = 0, vt8_bytes = 0;
-  float* scales = nullptr;    // [2][H][blocks]: block 0 = condition, 1 + s = slot s, last = current
-  uint32_t* amax = nullptr;   // [2][H] scratch of the quantiser
+  // Pool rows: condition rows [0, Lc), slot s at SlotTable::slot_row0(s, T, Lc)
+  // (starts rounded up to multiples of 8), then one spare slot at cur_row0 for
+  // the current chunk (V^T in bf16 caches, K and V codes in fp8 caches).
+  int64_t pool_rows;      // cur_row0: rows of the condition and the n_sink + W slots
+  int64_t spare_rows;     // pool_rows + round8(T)
+  void* k_pool = nullptr;  // bf16: K [H][pool_rows][D].  fp8: K codes [H][spare_rows][D]
+  void* v_pool = nullptr;  // bf16: V^T [H][D][spare_rows].  fp8: V^T codes [H][D][spare_rows]
+  size_t k_bytes = 0, v_bytes = 0;
+  float* scales = nullptr;    // fp8: [2][H][blocks]: block 0 = condition, 1 + s = slot s, last = current
+  uint32_t* amax = nullptr;   // fp8: [2][H] scratch of the quantiser
   int blocks() const { return n_sink + W + 2; }
-  int num_cus = 0;
-  float* ws_o = nullptr;   // attention workspace (partials of split query tiles)
-  float* ws_ml = nullptr;
-  int* ws_cnt = nullptr;
   kvc::SlotTable table;
-  int variant = 0;  // attention tiling (0 = default)
   kvc_cache(int T_, int W_, int S_, int Lc_, int H_, int D_, int dt)
       : T(T_), W(W_), n_sink(S_), Lc(Lc_), H(H_), D(D_), kv_dtype(dt), device(0),
-        pool_rows((int64_t)Lc_ + (int64_t)(S_ + W_) * T_), table(W_, S_) {}
+        pool_rows(kvc::SlotTable::slot_row0(S_ + W_, T_, Lc_)),
+        spare_rows(pool_rows + kvc::SlotTable::round8(T_)), table(W_, S_) {}
 };
 
 struct kvc_table {
@@ -69,8 +67,17 @@ namespace {
 // fp8 cache: quantise K/V bf16 [H][rows][D] into pool rows [row0, row0 + rows) with scale block blk.
 int quantize_into(kvc_cache* h, const void* k, const void* v, int rows, int row0, int blk, hipStream_t st) {
   return kvc::launch_quantize_fp8((const uint16_t*)k, (const uint16_t*)v, h->H, rows, h->D, h->amax,
-                                  (uint8_t*)h->k_pool, h->rows8 * h->D, (uint8_t*)h->v_pool, h->rows8, row0,
+                                  (uint8_t*)h->k_pool, h->spare_rows * h->D, (uint8_t*)h->v_pool, h->spare_rows, row0,
                                   h->scales + blk, h->H * h->blocks(), h->blocks(), st);
+}
+
+// bf16 cache: K rows copied to pool rows [row0, row0 + rows), V written transposed to columns row0...
+int write_bf16(kvc_cache* h, const void* k, const void* v, int rows, int row0, hipStream_t st) {
+  if (kvc::launch_rows_copy_bf16((const uint16_t*)k, (uint16_t*)h->k_pool, h->H, rows, h->D, h->pool_rows, row0,
+                                 st) != 0)
+    return -1;
+  return kvc::launch_transpose_v_bf16((const uint16_t*)v, (uint16_t*)h->v_pool, h->H, rows, h->D,
+                                      h->spare_rows, row0, st);
 }
 
 }  // namespace
@@ -99,9 +106,13 @@ int kv_cache_create(int chunk_tokens, int window_w, int n_sink, int cond_len, in
     return fail(KVC_ERR_UNSUPPORTED,
                 "kv_cache_create: fp8 caches need T and Lc multiples of 16 (got T=%d Lc=%d)", chunk_tokens,
                 cond_len);
-  const int64_t pool_rows = (int64_t)cond_len + (int64_t)(n_sink + window_w) * chunk_tokens;
-  if (pool_rows > INT32_MAX || (int64_t)chunk_tokens * heads > INT32_MAX)
-    return fail(KVC_ERR_INVALID, "kv_cache_create: sizes overflow 32-bit row indices");
+  // pool sizes (see kvc_cache), checked in 64 bits: each head's K and V^T must
+  // stay below 2^31 bytes (32-bit buffer offsets) and so must T * H rows
+  const int64_t T8 = ((int64_t)chunk_tokens + 7) & ~7LL, Lc8 = ((int64_t)cond_len + 7) & ~7LL;
+  const int64_t spare_rows = Lc8 + (int64_t)(n_sink + window_w + 1) * T8;
+  if (spare_rows * head_dim * 2 > INT32_MAX || (int64_t)chunk_tokens * heads * head_dim * 2 > INT32_MAX)
+    return fail(KVC_ERR_INVALID, "kv_cache_create: sizes overflow 32-bit offsets (T=%d Lc=%d slots=%d D=%d)",
+                chunk_tokens, cond_len, n_sink + window_w, head_dim);
   kvc_cache* c = new (std::nothrow) kvc_cache(chunk_tokens, window_w, n_sink, cond_len, heads,
                                               head_dim, kv_dtype);
   if (!c) return fail(KVC_ERR_OOM, "kv_cache_create: host allocation failed");
@@ -110,47 +121,34 @@ int kv_cache_create(int chunk_tokens, int window_w, int n_sink, int cond_len, in
     delete c;
     return hip_fail(e, "kv_cache_create: hipGetDevice");
   }
-  e = hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, c->device);
-  if (e != hipSuccess) {
-    delete c;
-    return hip_fail(e, "kv_cache_create: hipDeviceGetAttribute");
-  }
   const bool fp8 = kv_dtype == KVC_KV_FP8;
-  c->rows8 = pool_rows + chunk_tokens;
-  const size_t elem = fp8 ? 1 : 2;
-  // fp8 pools hold one more slot (the current chunk) and 64 spare bytes
-  const size_t bytes = fp8 ? (size_t)heads * (size_t)c->rows8 * (size_t)head_dim + 64
-                           : (size_t)heads * (size_t)pool_rows * (size_t)head_dim * elem;
-  if (fp8 && bytes > (size_t)INT32_MAX) {
+  const size_t hd = (size_t)heads * (size_t)head_dim;
+  // fp8 code pools carry 64 spare bytes past the last row (the fp8 kernel's loads are range-checked
+  // against the allocation, not per head)
+  c->k_bytes = fp8 ? hd * (size_t)c->spare_rows + 64 : hd * (size_t)c->pool_rows * 2;
+  c->v_bytes = fp8 ? hd * (size_t)c->spare_rows + 64 : hd * (size_t)c->spare_rows * 2;
+  if (fp8 && c->k_bytes > (size_t)INT32_MAX) {
     delete c;
-    return fail(KVC_ERR_INVALID, "kv_cache_create: fp8 code pool of %zu bytes exceeds 2^31", bytes);
+    return fail(KVC_ERR_INVALID, "kv_cache_create: fp8 code pool of %zu bytes exceeds 2^31", c->k_bytes);
   }
-  c->k8_bytes = c->vt8_bytes = fp8 ? bytes : 0;
-  const size_t n_cnt = (size_t)kvc::attention_max_units(chunk_tokens, heads);
-  e = hipMalloc(&c->k_pool, bytes);
-  if (e == hipSuccess) e = hipMalloc(&c->v_pool, bytes);
+  e = hipMalloc(&c->k_pool, c->k_bytes);
+  if (e == hipSuccess) e = hipMalloc(&c->v_pool, c->v_bytes);
   if (e == hipSuccess && fp8) e = hipMalloc(&c->scales, sizeof(float) * 2 * heads * c->blocks());
   if (e == hipSuccess && fp8) e = hipMalloc(&c->amax, sizeof(uint32_t) * 2 * heads);
   if (e == hipSuccess && fp8) e = hipMemset(c->scales, 0, sizeof(float) * 2 * heads * c->blocks());
-  if (e == hipSuccess) e = hipMalloc(&c->ws_o, kvc::attention_ws_o_bytes(c->num_cus));
-  if (e == hipSuccess) e = hipMalloc(&c->ws_ml, kvc::attention_ws_ml_bytes(c->num_cus));
-  if (e == hipSuccess) e = hipMalloc(&c->ws_cnt, n_cnt * sizeof(int));
-  // the pool starts as zeros (finite values everywhere), the counters at zero
-  if (e == hipSuccess) e = hipMemset(c->k_pool, 0, bytes);
-  if (e == hipSuccess) e = hipMemset(c->v_pool, 0, bytes);
-  if (e == hipSuccess) e = hipMemset(c->ws_cnt, 0, n_cnt * sizeof(int));
+  // the pool starts as zeros: finite values everywhere, zero padding between slots
+  if (e == hipSuccess) e = hipMemset(c->k_pool, 0, c->k_bytes);
+  if (e == hipSuccess) e = hipMemset(c->v_pool, 0, c->v_bytes);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
-    for (void* p : {(void*)c->k_pool, (void*)c->v_pool, (void*)c->ws_o, (void*)c->ws_ml, (void*)c->ws_cnt,
-                    (void*)c->scales, (void*)c->amax})
+    for (void* p : {(void*)c->k_pool, (void*)c->v_pool, (void*)c->scales, (void*)c->amax})
       if (p) (void)hipFree(p);
     (void)hipGetLastError();
     delete c;
     return fail(e == hipErrorOutOfMemory ? KVC_ERR_OOM : KVC_ERR_HIP,
-                "kv_cache_create: device allocation (pool 2 x %zu bytes + workspace) failed: %s", bytes,
-                hipGetErrorString(e));
+                "kv_cache_create: device allocation (pools of %zu + %zu bytes) failed: %s", c->k_bytes,
+                c->v_bytes, hipGetErrorString(e));
   }
-  if (const char* v = getenv("KVC_ATTN_VARIANT")) c->variant = atoi(v);
   *out = c;
   return KVC_OK;
 }
@@ -161,8 +159,7 @@ int kv_cache_destroy(kvc_handle h) {
   int rc = KVC_OK;
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) rc = hip_fail(e, "kv_cache_destroy: hipDeviceSynchronize");
-  for (void* p : {(void*)h->k_pool, (void*)h->v_pool, (void*)h->ws_o, (void*)h->ws_ml, (void*)h->ws_cnt,
-                  (void*)h->scales, (void*)h->amax})
+  for (void* p : {(void*)h->k_pool, (void*)h->v_pool, (void*)h->scales, (void*)h->amax})
     if (p) (void)hipFree(p);
   delete h;
   return rc;
@@ -178,9 +175,7 @@ int kv_cache_set_condition(kvc_handle h, const void* k_cond, const void* v_cond,
       return fail(KVC_ERR_HIP, "kv_cache_set_condition: launch failed");
     return KVC_OK;
   }
-  if (kvc::launch_pool_write_bf16((const uint16_t*)k_cond, (const uint16_t*)v_cond,
-                                  (uint16_t*)h->k_pool, (uint16_t*)h->v_pool, h->H, h->Lc, h->D,
-                                  h->pool_rows, 0, (hipStream_t)stream) != 0)
+  if (write_bf16(h, k_cond, v_cond, h->Lc, 0, (hipStream_t)stream) != 0)
     return fail(KVC_ERR_HIP, "kv_cache_set_condition: launch failed");
   return KVC_OK;
 }
@@ -193,12 +188,9 @@ int kv_cache_append_chunk(kvc_handle h, const void* k, const void* v, void* stre
   int slot;
   int64_t evicted;
   h->table.plan_append(&slot, &evicted);
-  const int row0 = h->Lc + slot * h->T;
-  const int rc = h->kv_dtype == KVC_KV_FP8
-                     ? quantize_into(h, k, v, h->T, row0, 1 + slot, (hipStream_t)stream)
-                     : kvc::launch_pool_write_bf16((const uint16_t*)k, (const uint16_t*)v, (uint16_t*)h->k_pool,
-                                                   (uint16_t*)h->v_pool, h->H, h->T, h->D, h->pool_rows, row0,
-                                                   (hipStream_t)stream);
+  const int row0 = kvc::SlotTable::slot_row0(slot, h->T, h->Lc);
+  const int rc = h->kv_dtype == KVC_KV_FP8 ? quantize_into(h, k, v, h->T, row0, 1 + slot, (hipStream_t)stream)
+                                           : write_bf16(h, k, v, h->T, row0, (hipStream_t)stream);
   if (rc != 0) return fail(KVC_ERR_HIP, "kv_cache_append_chunk: launch failed");
   const int64_t id = h->table.next_chunk_id();
   h->table.commit_append(slot);
@@ -254,15 +246,13 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
   a.o = (uint16_t*)o;
   a.lse = lse;
   a.kpool = (const uint16_t*)h->k_pool;
-  a.vpool = (const uint16_t*)h->v_pool;
-  a.pool_rows = h->pool_rows;
+  a.vt = (const uint16_t*)h->v_pool;
+  a.rows_k = h->pool_rows;
+  a.rows_v = h->spare_rows;
+  a.cur_row0 = (int)h->pool_rows;
   a.T = h->T;
   a.H = h->H;
   a.c = scale * 1.4426950408889634f;
-  a.num_cus = h->num_cus;
-  a.ws_o = h->ws_o;
-  a.ws_ml = h->ws_ml;
-  a.ws_cnt = h->ws_cnt;
   if (h->kv_dtype == KVC_KV_FP8) {
     // every chunk has its own scales: one segment per block, the current chunk
     // quantised into the spare slot after the window slots
@@ -270,12 +260,12 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
     if ((int)segs.size() + 1 > kvc::kMaxSegments)
       return fail(KVC_ERR_STATE, "sink_window_attention: %zu segments", segs.size());
     const int n_slots = h->n_sink + h->W;
-    const int cur_row0 = h->Lc + n_slots * h->T;
+    const int cur_row0 = (int)h->pool_rows;
     a.nseg = 0;
     for (const kvc::Segment& sg : segs) {
       a.seg_row0[a.nseg] = sg.row0;
       a.seg_len[a.nseg] = sg.len;
-      a.seg_blk[a.nseg] = sg.row0 < h->Lc ? 0 : 1 + (sg.row0 - h->Lc) / h->T;
+      a.seg_blk[a.nseg] = sg.row0 < h->Lc ? 0 : 1 + (sg.row0 - kvc::SlotTable::round8(h->Lc)) / kvc::SlotTable::round8(h->T);
       ++a.nseg;
     }
     a.seg_row0[a.nseg] = cur_row0;
@@ -284,9 +274,9 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
     ++a.nseg;
     a.k8 = (const uint8_t*)h->k_pool;
     a.vt8 = (const uint8_t*)h->v_pool;
-    a.k8_bytes = (int64_t)h->k8_bytes;
-    a.vt8_bytes = (int64_t)h->vt8_bytes;
-    a.pool_rows8 = h->rows8;
+    a.k8_bytes = (int64_t)h->k_bytes;
+    a.vt8_bytes = (int64_t)h->v_bytes;
+    a.pool_rows8 = h->spare_rows;
     a.scales = h->scales;
     a.scale_tensor = h->H * h->blocks();
     a.scale_head = h->blocks();
@@ -304,8 +294,12 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
     a.seg_row0[i] = segs[i].row0;
     a.seg_len[i] = segs[i].len;
   }
-  const int rc = kvc::launch_attention_bf16(a, h->D, h->variant, (hipStream_t)stream);
-  if (rc != 0) return fail(KVC_ERR_HIP, "sink_window_attention: launch failed");
+  // the current chunk's V goes transposed into the spare slot, then the attention kernel
+  if (kvc::launch_transpose_v_bf16((const uint16_t*)v_cur, (uint16_t*)h->v_pool, h->H, h->T, h->D, h->spare_rows,
+                                   (int)h->pool_rows, (hipStream_t)stream) != 0)
+    return fail(KVC_ERR_HIP, "sink_window_attention: transpose launch failed");
+  if (kvc::launch_attention_bf16(a, h->D, (hipStream_t)stream) != 0)
+    return fail(KVC_ERR_HIP, "sink_window_attention: launch failed");
   return KVC_OK;
 }
 
@@ -316,7 +310,7 @@ int kv_cache_pool_view(kvc_handle h, const void** k_pool, const void** v_pool, c
   if (k_pool) *k_pool = h->k_pool;
   if (v_pool) *v_pool = h->v_pool;
   if (scales) *scales = h->scales;
-  if (rows) *rows = h->kv_dtype == KVC_KV_FP8 ? h->rows8 : h->pool_rows;
+  if (rows) *rows = h->spare_rows;
   if (blocks) *blocks = h->kv_dtype == KVC_KV_FP8 ? h->blocks() : 0;
   return KVC_OK;
 }

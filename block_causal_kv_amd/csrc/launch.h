@@ -15,24 +15,15 @@ struct AttnArgs {
   const uint16_t* vcur;
   uint16_t* o;           // [H][T][D] bf16
   float* lse;            // [H][T] or null
-  const uint16_t* kpool; // [H][pool_rows][D]
-  const uint16_t* vpool;
-  int64_t pool_rows;
+  const uint16_t* kpool; // bf16 K pool [H][rows_k][D]
+  const uint16_t* vt;    // bf16 V pool, transposed: [H][D][rows_v]; the current chunk at cur_row0
+  int64_t rows_k;
+  int64_t rows_v;
+  int cur_row0;
   int T;
   int H;
   float c;  // softmax scale * log2(e)
   int q_tiles;
-  // persistent (stream-K) schedule: set by the launcher from num_cus
-  int num_cus;   // compute units of the device
-  int units;     // H * q_tiles
-  int tiles;     // key tiles per unit
-  int groups;    // persistent workgroups
-  int rounds;    // full rounds of whole units per workgroup
-  int rest;      // units left after the full rounds
-  int slices;    // key-range slices each rest unit is cut into
-  float* ws_o;   // partial O^T of sliced units: [num_cus][8 waves][16][64 lanes] float4
-  float* ws_ml;  // partial (max, sum): [num_cus][8][64] float2
-  int* ws_cnt;   // per-unit piece counters, zero between calls: [max units]
   int nseg;
   int32_t seg_row0[kMaxSegments];
   int32_t seg_len[kMaxSegments];
@@ -49,21 +40,18 @@ struct AttnArgs {
   int32_t seg_blk[kMaxSegments];
 };
 
-// Workspace of the persistent attention kernel, per cache: bytes of ws_o and ws_ml,
-// and the number of counters (units).
-size_t attention_ws_o_bytes(int num_cus);
-size_t attention_ws_ml_bytes(int num_cus);
-int attention_max_units(int T, int H);
+// bf16 attention: one workgroup per (head, 128-row query tile), two per CU.
+int launch_attention_bf16(AttnArgs& a, int head_dim, hipStream_t stream);
 
-// variant: 0 = default (one workgroup per 128-row query tile, two per CU);
-// 2 = persistent ping-pong kernel with the rounds + slices schedule.
-int launch_attention_bf16(AttnArgs& a, int head_dim, int variant, hipStream_t stream);
+// Copy K src [H][rows][D] (bf16) into rows [row0, row0 + rows) of a pool [H][pool_rows][D].
+int launch_rows_copy_bf16(const uint16_t* src, uint16_t* pool, int H, int rows, int D, int64_t pool_rows,
+                          int row0, hipStream_t stream);
 
-// Copy src [H][rows][D] (bf16) into dst rows [row0, row0 + rows) of a pool
-// [H][pool_rows][D], for K and V in one launch.
-int launch_pool_write_bf16(const uint16_t* k_src, const uint16_t* v_src, uint16_t* k_pool,
-                           uint16_t* v_pool, int H, int rows, int D, int64_t pool_rows, int row0,
-                           hipStream_t stream);
+// Write V src [H][rows][D] (bf16) transposed into columns [col0, col0 + rows) of
+// vt [H][D][vt_rows]; col0 and vt_rows are multiples of 8, and the columns up to
+// the next multiple of 8 are written with zeros.
+int launch_transpose_v_bf16(const uint16_t* src, uint16_t* vt, int H, int rows, int D, int64_t vt_rows,
+                            int col0, hipStream_t stream);
 
 // fp8 attention (E4M3 K/V codes, per-(head, chunk) scales).
 int launch_attention_fp8(AttnArgs& a, int head_dim, hipStream_t stream);

@@ -52,19 +52,14 @@ void SlotTable::evict(int n, int64_t* ids) {
 std::vector<Segment> SlotTable::segments(int chunk_tokens, int cond_len, bool merge) const {
   std::vector<Segment> out;
   if (cond_len > 0) out.push_back({0, cond_len, -1});
-  bool prev_open = cond_len > 0;  // the condition rows end where slot 0 begins
   for (int s = 0; s < n_slots(); ++s) {
-    if (slots_[s] < 0) {
-      prev_open = false;
-      continue;
-    }
-    int32_t row0 = cond_len + s * chunk_tokens;
-    if (merge && prev_open && !out.empty() && out.back().row0 + out.back().len == row0) {
+    if (slots_[s] < 0) continue;
+    const int32_t row0 = slot_row0(s, chunk_tokens, cond_len);
+    if (merge && !out.empty() && out.back().row0 + out.back().len == row0) {
       out.back().len += chunk_tokens;
     } else {
       out.push_back({row0, chunk_tokens, static_cast<int32_t>(slots_[s])});
     }
-    prev_open = true;
   }
   return out;
 }

@@ -14,7 +14,7 @@
 namespace kvc {
 
 struct Segment {
-  int32_t row0;  // first pool row (pool rows: [0, Lc) condition, then slot s at Lc + s*T)
+  int32_t row0;  // first pool row (rows [0, Lc) condition, slot s at slot_row0(s, T, Lc))
   int32_t len;   // rows
   int32_t chunk; // chunk id held in the first slot of the run (-1: condition only)
 };
@@ -42,6 +42,15 @@ class SlotTable {
   // condition rows and every occupied slot.  With merge, physically adjacent
   // runs (condition rows and consecutive occupied slots) become one segment.
   std::vector<Segment> segments(int chunk_tokens, int cond_len, bool merge) const;
+
+  // Pool layout: the condition rows, then one slot of T rows per chunk; the
+  // condition block and every slot start on a multiple of 8 rows (the rows in
+  // between are padding), so 8-row pieces of a slot are 16-byte aligned in a
+  // transposed bf16 pool.
+  static int32_t round8(int32_t x) { return (x + 7) & ~7; }
+  static int32_t slot_row0(int slot, int chunk_tokens, int cond_len) {
+    return round8(cond_len) + slot * round8(chunk_tokens);
+  }
 
  private:
   int window_, n_sink_;

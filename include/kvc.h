@@ -68,10 +68,13 @@ const char* kvc_last_error(void);
  *   heads         H >= 1;  head_dim D in {64, 128}
  *   kv_dtype      KVC_KV_BF16 or KVC_KV_FP8 (fp8 needs T and Lc multiples of 16)
  *   out           receives the handle
- * Pool: K and V each [H][Lc + (n_sink + W) * T][D] (bf16, or 1-byte codes),
- * plus, for fp8, scales and a staging slot for the current chunk.  No device
- * memory is allocated by any later call.  Errors: INVALID, UNSUPPORTED, OOM
- * (nothing allocated, *out untouched), HIP.
+ * Pool rows: the condition rows [0, Lc), then slot s (s < n_sink + W) at
+ * round8(Lc) + s * round8(T) (round8 = round up to a multiple of 8; padding rows
+ * stay zero), then one spare slot for the current chunk.  K is stored
+ * row-major per head, V transposed per head (see kv_cache_pool_view); fp8
+ * caches hold 1-byte codes plus one scale per (head, chunk).  No device memory
+ * is allocated by any later call.  Errors: INVALID (also: a head's pool would
+ * exceed 2^31 bytes), UNSUPPORTED, OOM (nothing allocated, *out untouched), HIP.
  */
 int kv_cache_create(int chunk_tokens, int window_w, int n_sink, int cond_len, int heads,
                     int head_dim, int kv_dtype, kvc_handle* out);
@@ -139,8 +142,10 @@ int kv_cache_query(kvc_handle h, int64_t* next_chunk_id, int* occupancy, int64_t
  *   scale            softmax scale; <= 0 selects 1/sqrt(D)
  * For query i of head h: o_i = sum_j softmax_j(scale * q_i . k_j) v_j over the
  * keys j of the condition tokens, every chunk resident in the cache, and the
- * chunk's own T tokens.  fp8 mode: k_cur/v_cur are quantised like an append
- * (per-head scale) before use.  Errors: INVALID, HIP.
+ * chunk's own T tokens.  The call first writes v_cur (bf16: transposed; fp8:
+ * k_cur too, quantised like an append with per-head scales) into the pool's
+ * spare slot, so two calls on one cache must not run concurrently.
+ * Errors: INVALID, HIP.
  */
 int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const void* v_cur,
                           void* o, float* lse, float scale, void* stream);
@@ -148,13 +153,15 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
 /*
  * kv_cache_pool_view - device addresses of the pool, for inspection (tests,
  * tools).  Read-only use; valid until destroy.  Any output may be NULL.
- *   k_pool   bf16: K [H][rows][D].  fp8: K codes [H][rows][D] (1 byte each)
- *   v_pool   bf16: V [H][rows][D].  fp8: V codes transposed, [H][D][rows]
+ *   rows     pool rows including the spare slot: round8(Lc) + (n_sink + W + 1) *
+ *            round8(T); slot s starts at row round8(Lc) + s * round8(T), the spare
+ *            slot (the current chunk of the last attention call) at rows - round8(T)
+ *   k_pool   bf16: K [H][rows - round8(T)][D] (no spare slot: the call reads k_cur).
+ *            fp8: K codes [H][rows][D] (1 byte each)
+ *   v_pool   bf16: V transposed, [H][D][rows].  fp8: V codes transposed, [H][D][rows]
  *   scales   fp8: float32 [2 (K, V)][H][blocks]; block 0 = condition rows,
  *            1 + s = slot s, blocks - 1 = the current chunk of the last
  *            attention call.  NULL for bf16.
- *   rows     pool rows: Lc + (n_sink + W) * T (bf16) or Lc + (n_sink + W + 1) * T
- *            (fp8: one more slot for the current chunk); slot s starts at Lc + s*T
  *   blocks   fp8: n_sink + W + 2; bf16: 0
  */
 int kv_cache_pool_view(kvc_handle h, const void** k_pool, const void** v_pool, const float** scales,
@@ -177,8 +184,8 @@ int kvc_table_query(kvc_table_handle t, int64_t* next_chunk_id, int* occupancy,
 /*
  * kvc_table_segments - the key segments (pool rows) a query of the next chunk
  * reads from the pool: the condition rows [0, Lc) and each occupied slot s at
- * rows [Lc + s*T, Lc + (s+1)*T); with merge != 0, physically adjacent runs are
- * joined.  The chunk's own rows are not part of the pool and not listed.
+ * rows [r, r + T), r = round8(Lc) + s * round8(T); with merge != 0, physically
+ * adjacent runs are joined (only possible where T and Lc are multiples of 8).  The chunk's own rows are not part of the pool and not listed.
  * row0/len receive up to cap entries; *n_out the count (which may exceed cap:
  * then INVALID).
  */

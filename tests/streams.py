@@ -50,7 +50,7 @@ def say(*a):
 
 
 def run_stream(spec: synthetic.StreamSpec, check: Iterable[int], rows: Optional[np.ndarray] = None,
-               evict_plan: Optional[Dict[int, int]] = None, variant_env: Optional[str] = None,
+               evict_plan: Optional[Dict[int, int]] = None,
                max_abs: float = BF16_MAX_ABS, rel_l2: float = BF16_REL_L2, lse_tol: float = LSE_TOL):
     """Run chunks 0..max(check) of ``spec``; compare attention at the chunks in
     ``check`` (every step, the given rows or all) and every append's indices."""

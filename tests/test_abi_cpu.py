@@ -74,6 +74,10 @@ def test_slot_table_closed_form_without_manual_eviction(W, S):
         assert t.query()["occupancy"] == min(c + 1, S + W)
 
 
+def _round8(x):
+    return (x + 7) // 8 * 8
+
+
 def _rows_of_segments(segs):
     rows = set()
     for r0, n in segs:
@@ -82,9 +86,10 @@ def _rows_of_segments(segs):
 
 
 @pytest.mark.parametrize("merge", [True, False])
-def test_segments_cover_exactly_the_visible_chunks(merge):
+@pytest.mark.parametrize("T,Lc", [(5, 3), (8, 16), (16, 0)])
+def test_segments_cover_exactly_the_visible_chunks(merge, T, Lc):
     from block_causal_kv_amd import SlotTable
-    T, Lc, W, S = 5, 3, 3, 1
+    W, S = 3, 1
     t, m = SlotTable(W, S), CacheModel(W, S)
     rng = np.random.default_rng(5)
     for step in range(60):
@@ -94,8 +99,9 @@ def test_segments_cover_exactly_the_visible_chunks(merge):
         segs = t.segments(T, Lc, merge)
         want = set(range(Lc))
         for slot, c in enumerate(m.slot_map()):
-            if c >= 0:
-                want.update(range(Lc + slot * T, Lc + (slot + 1) * T))
+            if c >= 0:  # pool layout: slot starts rounded up to multiples of 8 rows
+                r0 = _round8(Lc) + slot * _round8(T)
+                want.update(range(r0, r0 + T))
         assert _rows_of_segments(segs) == want
         assert sum(n for _, n in segs) == len(want)  # no row twice
         if merge:  # adjacent runs are joined

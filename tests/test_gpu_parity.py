@@ -62,21 +62,50 @@ def test_720p_sampled_rows():
     run_stream(spec, [0, 1, W, W + 1, W + 2, spec.n_chunks - 1], rows=rows)
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid"])
-def test_persistent_kernel_variant(name, monkeypatch):
-    """The persistent ping-pong kernel (rounds of whole query tiles, then aligned
-    key-range slices merged by the last slice) against the oracle."""
-    monkeypatch.setenv("KVC_ATTN_VARIANT", "2")
-    spec = synthetic.SPECS[name]
-    say("persistent kernel,", name)
-    run_stream(spec, range(spec.n_chunks))
-
-
-def test_persistent_kernel_sliced_units(monkeypatch):
-    """A shape whose leftover query tiles are cut into key-range slices (H*ceil(T/256)
-    not a multiple of the CU count), with a ragged tail and two steps."""
-    monkeypatch.setenv("KVC_ATTN_VARIANT", "2")
-    spec = synthetic.small_spec("sliced", n_chunks=5, chunk_tokens=600, cond_len=40, heads=6, head_dim=128,
+def test_multi_head_ragged_two_steps():
+    """Several query tiles per head with a ragged last one, condition rows not a
+    multiple of 8 and chunks of 604 rows (padded pool layout), two steps with separate clean K/V."""
+    spec = synthetic.small_spec("ragged_multi", n_chunks=5, chunk_tokens=604, cond_len=44, heads=6, head_dim=128,
                                 window=2, steps=2, clean_from_last_step=False, outlier_frac=0.01, seed=17)
-    say("persistent kernel, sliced units", spec)
+    say("multi-head ragged stream", spec)
     run_stream(spec, range(spec.n_chunks))
+
+
+def test_evicted_nonfinite_chunk_does_not_leak():
+    """A window chunk holding NaN keys and infinite values is evicted.  The last,
+    partial tile of the sink chunk before it covers pool rows past the sink
+    (padding, then the evicted slot); nothing of those rows may reach the output."""
+    import torch
+    from block_causal_kv_amd import KVCache
+    from oracle.cache import CacheModel
+    from oracle.stream import attend_chunk
+    from streams import errors, from_dev, to_dev, BF16_MAX_ABS, BF16_REL_L2
+
+    spec = synthetic.small_spec("nonfinite", n_chunks=3, chunk_tokens=100, cond_len=4, heads=2, head_dim=128,
+                                window=2, seed=18)
+    H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
+    cache = KVCache(T, spec.window, spec.n_sink, spec.cond_len, H, D, "bf16")
+    model = CacheModel(spec.window, spec.n_sink)
+    ck, cv = synthetic.cond_inputs(spec)
+    cache.set_condition(to_dev(ck), to_dev(cv))
+    x0 = synthetic.chunk_inputs(spec, 0, clean_only=True)
+    assert cache.append_chunk(to_dev(x0.k_clean), to_dev(x0.v_clean)) == model.append()  # sink slot
+    bad_k = np.full((H, T, D), np.nan)
+    bad_v = np.full((H, T, D), np.inf)
+    assert cache.append_chunk(to_dev(bad_k), to_dev(bad_v)) == model.append()  # window slot
+    assert cache.evict(1) == model.evict(1)
+    x2 = synthetic.chunk_inputs(spec, 2)
+    o = cache.attention(to_dev(x2.q[0]), to_dev(x2.k[0]), to_dev(x2.v[0]))
+    torch.cuda.synchronize()
+    got = from_dev(o)
+    # the oracle masks the evicted chunk out; it is given zeros there (its
+    # result does not depend on keys it masks)
+    zeros = np.zeros((H, T, D))
+    clean = {0: x0.k_clean, 1: zeros}, {0: x0.v_clean, 1: zeros}
+    ref, _ = attend_chunk(2, x2.q[0], x2.k[0], x2.v[0], clean[0].__getitem__, clean[1].__getitem__, ck, cv,
+                          spec.window, spec.n_sink, spec.scale, visible=model.resident())
+    assert np.isfinite(got).all()
+    ma, rl = errors(got, ref)
+    say("  non-finite neighbour: max_abs %.3e rel_l2 %.3e" % (ma, rl))
+    assert ma <= BF16_MAX_ABS and rl <= BF16_REL_L2
+    cache.close()
