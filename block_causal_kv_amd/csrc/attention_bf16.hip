@@ -28,6 +28,15 @@
 //   share each CU, so every SIMD holds two waves of independent workgroups and
 //   one wave's MFMAs overlap the other's softmax arithmetic.
 //
+// Work split
+//   The (head, query tile) units fill the CUs' workgroup slots in rounds.  When
+//   the last round would be partly empty, its units are each cut into a few
+//   aligned key-tile ranges (slices) run by separate workgroups: every slice
+//   leaves its unnormalised O^T, running max and partial sums in a workspace,
+//   and the slice that finishes last (device-scope counter, no waiting) merges
+//   them and writes the output.  Slices of one index of the same head's tiles
+//   go to one XCD, so they stream the same K/V through its L2.
+//
 // LDS tiles (one direct load writes 64 lanes x 16 bytes contiguously)
 //   K tile: 64 rows x D, row r at r * 2D bytes; its 16-byte granule g is stored
 //   at position g ^ swz_k(r).  V^T tile: D rows of 64 keys (128 bytes), key
@@ -81,6 +90,7 @@ struct Cfg {
   static constexpr int DB = D / 32;          // 32-wide output blocks over the head dim
   static constexpr int KB = BN / 32;         // 32-key blocks per tile
   static_assert(TILE_B % (1024 * NW) == 0, "tile must split into whole 1 KB loads per wave");
+  static_assert(2 * LPW == DS, "the next tile's loads are spread one per k-step of S^T");
 };
 
 // Granule swizzles (see header): rows that share bank groups get different
@@ -104,31 +114,49 @@ __device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
 }
 
 // 16 bytes per lane from a buffer resource straight into LDS at lds_byte + 16 * lane.
-// Written as inline assembly so the compiler does not order the kernel's LDS
-// reads after it (it cannot tell which LDS bytes the load writes, and would
-// wait for it before the first read of the other buffer).  Completion is
-// awaited explicitly (s_waitcnt vmcnt(0)) before the barrier that publishes
-// the tile.  M0 holds the LDS address.
+// Written as inline assembly so the compiler neither waits for it before the
+// kernel's LDS reads (it cannot tell which LDS bytes the load writes) nor keeps
+// those reads from moving past it: the load always writes the buffer that no
+// wave reads until the next barrier.  Completion is awaited explicitly
+// (s_waitcnt vmcnt(0)) before that barrier.  M0 holds the LDS address.
 __device__ __forceinline__ void load_lds16(u32x4 r, uint32_t lds_byte, uint32_t voff, uint32_t soff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(lds_byte), "v"(voff), "s"(r), "s"(soff)
-               : "memory", "m0");
+               : "m0");
 }
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::BUF_B];
+  __shared__ int s_last;
 
-  // XCD-aware unit mapping: workgroup b runs on XCD b % 8; give each XCD a
-  // contiguous range of units so the query tiles of one head share that XCD's L2.
-  const int units = a.H * a.q_tiles;
-  const int per_xcd = (units + 7) / 8;
-  const int xcd = blockIdx.x % 8;
-  const int k_in = blockIdx.x / 8;
-  const int unit = xcd * per_xcd + k_in;
-  if (k_in >= per_xcd || unit >= units) return;
+  // Work item.  Workgroup b runs on XCD b % 8 (both parts of the grid start on
+  // a multiple of 8); each XCD gets a contiguous range of items, so the query
+  // tiles of one head share that XCD's L2.
+  int unit, t0 = 0, t1 = a.tiles, piece = -1, ru = 0;
+  {
+    const int b = blockIdx.x;
+    const int xcd = b % 8;
+    if (b < a.grid_whole) {
+      const int per_xcd = (a.n_whole + 7) / 8;
+      const int k_in = b / 8;
+      unit = xcd * per_xcd + k_in;
+      if (k_in >= per_xcd || unit >= a.n_whole) return;
+    } else {
+      const int n_pieces = a.rest * a.slices;
+      const int per_xcd = (n_pieces + 7) / 8;
+      const int k_in = (b - a.grid_whole) / 8;
+      piece = xcd * per_xcd + k_in;
+      if (k_in >= per_xcd || piece >= n_pieces) return;
+      const int slice = piece / a.rest;
+      ru = piece % a.rest;
+      unit = a.n_whole + ru;
+      t0 = (int)((int64_t)slice * a.tiles / a.slices);
+      t1 = (int)((int64_t)(slice + 1) * a.tiles / a.slices);
+    }
+  }
   const int head = unit / a.q_tiles;
   const int qtile = unit % a.q_tiles;
 
@@ -213,34 +241,49 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
     return cur;
   };
 
-  // ---- tile producer: this wave's share of the tile's 1 KB blocks, into buffer buf
-  auto issue = [&](Cursor cur, int buf) {
+  // ---- tile producer: this wave's share of the tile's 1 KB blocks (LPW of K,
+  // LPW of V^T) into buffer buf.  The loads are issued one at a time between
+  // the MFMAs of the previous tile, so the memory pipeline is fed steadily
+  // instead of in a burst that stalls every wave at issue.
+  struct Plan {
+    u32x4 rk;
+    uint32_t kso, vso, kdst, vdst;
+    uint32_t vo[C::LPW];
+  };
+  auto make_plan = [&](Cursor cur, int buf) -> Plan {
+    Plan p;
     const int s = uniform(cur.seg);
     const bool in_pool = s < a.nseg;
     const int valid = min(C::BN, cur.len - cur.off);
     const int row0 = (in_pool ? a.seg_row0[s] : 0) + cur.off;        // K row of the tile's first key
     const int vcol0 = (in_pool ? a.seg_row0[s] : a.cur_row0) + cur.off;  // its V^T column
-    const uint32_t kso = (uint32_t)(row0 * C::RB), vso = (uint32_t)(vcol0 * 2);
-    const uint32_t bofs = (uint32_t)(buf * C::BUF_B);
-    const u32x4 rk = make_rsrc(in_pool ? kpool_h : kcur_h, in_pool ? kpool_bytes : kcur_bytes);
-#pragma unroll
-    for (int j = 0; j < C::LPW; ++j) load_lds16(rk, kblk + bofs + j * 1024, kvo[j], kso);
+    p.kso = (uint32_t)uniform(row0 * C::RB);
+    p.vso = (uint32_t)uniform(vcol0 * 2);
+    p.rk = make_rsrc(in_pool ? kpool_h : kcur_h, in_pool ? kpool_bytes : kcur_bytes);
+    p.kdst = (uint32_t)uniform((int)(kblk + buf * C::BUF_B));
+    p.vdst = (uint32_t)uniform((int)(vblk + buf * C::BUF_B));
     // V^T granules wholly past the segment read as zero, so no stale value of a
     // neighbouring slot meets a zero probability (0 * inf would be NaN).
-    if (valid == C::BN) {
 #pragma unroll
-      for (int j = 0; j < C::LPW; ++j) load_lds16(rv, vblk + bofs + j * 1024, vvo[j], vso);
-    } else {
-#pragma unroll
-      for (int j = 0; j < C::LPW; ++j)
-        load_lds16(rv, vblk + bofs + j * 1024, vkey[j] < valid ? vvo[j] : kOutOfRange, vso);
-    }
+    for (int j = 0; j < C::LPW; ++j) p.vo[j] = vkey[j] < valid ? vvo[j] : kOutOfRange;
+    return p;
+  };
+  auto load_one = [&](const Plan& p, int i) {  // i < LPW: K block i, else V^T block i - LPW
+    if (i < C::LPW)
+      load_lds16(p.rk, p.kdst + i * 1024, kvo[i], p.kso);
+    else
+      load_lds16(rv, p.vdst + (i - C::LPW) * 1024, p.vo[i - C::LPW], p.vso);
   };
 
   // ---- one key tile from LDS buffer BUF
-  auto compute = [&](auto buf_tag, int valid) {
+  auto compute = [&](auto buf_tag, int valid, const Plan& nplan, bool more) {
     constexpr int BUF = decltype(buf_tag)::value;
-    if (!wave_active) return;
+    if (!wave_active) {
+      if (more)
+#pragma unroll
+        for (int i = 0; i < 2 * C::LPW; ++i) load_one(nplan, i);
+      return;
+    }
     const uint8_t* kl = lds + BUF * C::BUF_B;
     // ---- S^T = K . Q^T
     f32x16 sacc[C::KB];
@@ -255,6 +298,7 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
         const uint4 raw = *(const uint4*)(kl + kaddr[ds] + kb * 32 * C::RB);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw), qreg[ds],
                                                             sacc[kb], 0, 0, 0);
+        if (kb == C::KB - 1 && more) load_one(nplan, ds);  // one load per k-step (2 LPW == DS)
       }
     // ---- mask the tail of a partial tile: key of register r = kb*32 + 16*(r/8) + 8*hf + r%8
     if (valid < C::BN) {
@@ -313,32 +357,85 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
       }
   };
 
-  // ---- main loop, unrolled by two so each half reads a fixed buffer.  At the
-  // top of a step the tile in buffer `buf` is complete in LDS (barrier) and the
-  // other buffer's previous tile has been read by every wave (same barrier), so
-  // the next tile's loads go there while this tile is computed.
-  const int nseg_total = a.nseg + 1;  // + the current chunk
-  Cursor cur = {0, 0, seg_len(0)};
-  issue(cur, 0);
+  // ---- main loop over key tiles [t0, t1), unrolled by two so each half reads
+  // a fixed buffer.  At the top of a step the tile in buffer `buf` is complete
+  // in LDS (barrier) and the other buffer's previous tile has been read by
+  // every wave (same barrier), so the next tile's loads go there while this
+  // tile is computed.
+  Cursor cur;
+  {
+    int rem = t0, sg = 0;
+    for (;;) {  // segment holding tile t0 (t0 < tiles, so this ends)
+      const int len = seg_len(sg);
+      const int nt = (len + C::BN - 1) / C::BN;
+      if (rem < nt) {
+        cur = {sg, rem * C::BN, len};
+        break;
+      }
+      rem -= nt;
+      ++sg;
+    }
+  }
+  int left = uniform(t1 - t0);  // >= 1
+  {
+    const Plan p0 = make_plan(cur, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * C::LPW; ++i) load_one(p0, i);
+  }
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   for (;;) {
-    Cursor nxt = advance(cur);
-    bool more = nxt.seg < nseg_total;
-    if (more) issue(nxt, 1);
-    compute(std::integral_constant<int, 0>(), min(C::BN, cur.len - cur.off));
+    Cursor nxt = cur;
+    bool more = --left > 0;
+    if (more) nxt = advance(cur);
+    compute(std::integral_constant<int, 0>(), min(C::BN, cur.len - cur.off), make_plan(nxt, 1), more);
     if (!more) break;
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     cur = nxt;
-    nxt = advance(cur);
-    more = nxt.seg < nseg_total;
-    if (more) issue(nxt, 0);
-    compute(std::integral_constant<int, 1>(), min(C::BN, cur.len - cur.off));
+    more = --left > 0;
+    if (more) nxt = advance(cur);
+    compute(std::integral_constant<int, 1>(), min(C::BN, cur.len - cur.off), make_plan(nxt, 0), more);
     if (!more) break;
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     cur = nxt;
+  }
+
+  // ---- a slice of a split unit: leave the partial result; the last slice merges
+  if (piece >= 0) {
+    constexpr int NR = C::DB * 16;  // O^T registers per lane
+    float* po = a.ws_o + (size_t)(piece * C::NW + wave) * NR * 64 + lane;
+    float* pml = a.ws_ml + (size_t)(piece * C::NW + wave) * 2 * 64 + lane;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) po[(db * 16 + r) * 64] = oacc[db][r];
+    pml[0] = m_run;
+    pml[64] = l_run;
+    __threadfence();  // publish the partial before counting this slice done
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&a.ws_cnt[ru], 1) == a.slices - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();  // see every other slice's partial
+    const int my_slice = piece / a.rest;
+    for (int j = 0; j < a.slices; ++j) {
+      if (j == my_slice) continue;
+      const size_t pj = (size_t)(j * a.rest + ru) * C::NW + wave;
+      const float* qo = a.ws_o + pj * NR * 64 + lane;
+      const float* qml = a.ws_ml + pj * 2 * 64 + lane;
+      const float mj = qml[0], lj = qml[64];
+      const float mm = fmaxf(m_run, mj);
+      const float a0 = __builtin_amdgcn_exp2f(m_run - mm), a1 = __builtin_amdgcn_exp2f(mj - mm);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a0 + qo[(db * 16 + r) * 64] * a1;
+      l_run = l_run * a0 + lj * a1;
+      m_run = mm;
+    }
+    if (tid == 0) a.ws_cnt[ru] = 0;  // ready for the next call
   }
 
   // ---- epilogue: O = O^T / l, bf16; lane holds dims db*32 + 8*(r/4) + 4*hf + r%4
@@ -358,17 +455,57 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
   }
 }
 
+constexpr int kWgPerCu = 2;      // workgroups resident per CU (registers and LDS)
+constexpr int kMaxSlices = 8;
+
 template <int D>
 int launch_cfg(AttnArgs& a, hipStream_t stream) {
   using C = Cfg<D>;
   a.q_tiles = (a.T + C::ROWS - 1) / C::ROWS;
+  a.q_rows = C::ROWS;
   const int units = a.H * a.q_tiles;
-  const int grid = 8 * ((units + 7) / 8);
+  int tiles = (a.T + C::BN - 1) / C::BN;
+  for (int s = 0; s < a.nseg; ++s) tiles += (a.seg_len[s] + C::BN - 1) / C::BN;
+  a.tiles = tiles;
+  // Split the units of the last, partly filled round of workgroup slots into
+  // key slices when that shortens it: a round of pieces 1/s as long costs
+  // ceil(rest * s / slots) / s of a whole round (plus a small merge cost).
+  const int slots = kWgPerCu * a.num_cus;
+  const int rest = units % slots;
+  int slices = 1;
+  double best = rest == 0 ? 0.0 : 1.0;  // (full rounds need no split)
+  for (int s = 2; s <= kMaxSlices && s <= tiles && rest * s <= attention_ws_counters(a.num_cus) * 2; ++s) {
+    const double cost = (double)((rest * s + slots - 1) / slots) / s + 0.02 * s;
+    if (cost < best) {
+      best = cost;
+      slices = s;
+    }
+  }
+  if (slices > 1 && a.ws_o != nullptr) {
+    a.rest = rest;
+    a.slices = slices;
+    a.n_whole = units - rest;
+  } else {
+    a.rest = 0;
+    a.slices = 1;
+    a.n_whole = units;
+  }
+  a.grid_whole = 8 * ((a.n_whole + 7) / 8);
+  const int grid = a.grid_whole + 8 * ((a.rest * a.slices + 7) / 8);
   hipLaunchKernelGGL((attention_bf16_kernel<D>), dim3(grid), dim3(C::NT), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace
+
+// The split pieces number at most 2 x (slots): rest < slots and rest * slices <= 2 * slots.
+int attention_ws_counters(int num_cus) { return kWgPerCu * num_cus; }
+size_t attention_ws_o_bytes(int num_cus, int head_dim) {
+  return (size_t)2 * attention_ws_counters(num_cus) * 4 * (head_dim / 32) * 16 * 64 * sizeof(float);
+}
+size_t attention_ws_ml_bytes(int num_cus) {
+  return (size_t)2 * attention_ws_counters(num_cus) * 4 * 2 * 64 * sizeof(float);
+}
 
 int launch_attention_bf16(AttnArgs& a, int head_dim, hipStream_t stream) {
   if (head_dim == 128) return launch_cfg<128>(a, stream);

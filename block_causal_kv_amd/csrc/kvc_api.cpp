@@ -50,6 +50,10 @@ struct kvc_cache {
   float* scales = nullptr;    // fp8: [2][H][blocks]: block 0 = condition, 1 + s = slot s, last = current
   uint32_t* amax = nullptr;   // fp8: [2][H] scratch of the quantiser
   int blocks() const { return n_sink + W + 2; }
+  int num_cus = 0;
+  float* ws_o = nullptr;   // bf16 attention workspace: partials of split query tiles
+  float* ws_ml = nullptr;
+  int* ws_cnt = nullptr;
   kvc::SlotTable table;
   kvc_cache(int T_, int W_, int S_, int Lc_, int H_, int D_, int dt)
       : T(T_), W(W_), n_sink(S_), Lc(Lc_), H(H_), D(D_), kv_dtype(dt), device(0),
@@ -121,6 +125,11 @@ int kv_cache_create(int chunk_tokens, int window_w, int n_sink, int cond_len, in
     delete c;
     return hip_fail(e, "kv_cache_create: hipGetDevice");
   }
+  e = hipDeviceGetAttribute(&c->num_cus, hipDeviceAttributeMultiprocessorCount, c->device);
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(e, "kv_cache_create: hipDeviceGetAttribute");
+  }
   const bool fp8 = kv_dtype == KVC_KV_FP8;
   const size_t hd = (size_t)heads * (size_t)head_dim;
   // fp8 code pools carry 64 spare bytes past the last row (the fp8 kernel's loads are range-checked
@@ -128,26 +137,34 @@ int kv_cache_create(int chunk_tokens, int window_w, int n_sink, int cond_len, in
   c->k_bytes = fp8 ? hd * (size_t)c->spare_rows + 64 : hd * (size_t)c->pool_rows * 2;
   c->v_bytes = fp8 ? hd * (size_t)c->spare_rows + 64 : hd * (size_t)c->spare_rows * 2;
   if (fp8 && c->k_bytes > (size_t)INT32_MAX) {
+    const size_t kb = c->k_bytes;
     delete c;
-    return fail(KVC_ERR_INVALID, "kv_cache_create: fp8 code pool of %zu bytes exceeds 2^31", c->k_bytes);
+    return fail(KVC_ERR_INVALID, "kv_cache_create: fp8 code pool of %zu bytes exceeds 2^31", kb);
   }
   e = hipMalloc(&c->k_pool, c->k_bytes);
   if (e == hipSuccess) e = hipMalloc(&c->v_pool, c->v_bytes);
   if (e == hipSuccess && fp8) e = hipMalloc(&c->scales, sizeof(float) * 2 * heads * c->blocks());
   if (e == hipSuccess && fp8) e = hipMalloc(&c->amax, sizeof(uint32_t) * 2 * heads);
   if (e == hipSuccess && fp8) e = hipMemset(c->scales, 0, sizeof(float) * 2 * heads * c->blocks());
+  const int n_cnt = kvc::attention_ws_counters(c->num_cus);
+  if (e == hipSuccess && !fp8) e = hipMalloc(&c->ws_o, kvc::attention_ws_o_bytes(c->num_cus, head_dim));
+  if (e == hipSuccess && !fp8) e = hipMalloc(&c->ws_ml, kvc::attention_ws_ml_bytes(c->num_cus));
+  if (e == hipSuccess && !fp8) e = hipMalloc(&c->ws_cnt, n_cnt * sizeof(int));
+  if (e == hipSuccess && !fp8) e = hipMemset(c->ws_cnt, 0, n_cnt * sizeof(int));  // counters start at zero
   // the pool starts as zeros: finite values everywhere, zero padding between slots
   if (e == hipSuccess) e = hipMemset(c->k_pool, 0, c->k_bytes);
   if (e == hipSuccess) e = hipMemset(c->v_pool, 0, c->v_bytes);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
-    for (void* p : {(void*)c->k_pool, (void*)c->v_pool, (void*)c->scales, (void*)c->amax})
+    for (void* p : {(void*)c->k_pool, (void*)c->v_pool, (void*)c->scales, (void*)c->amax, (void*)c->ws_o,
+                    (void*)c->ws_ml, (void*)c->ws_cnt})
       if (p) (void)hipFree(p);
     (void)hipGetLastError();
+    const size_t kb = c->k_bytes, vb = c->v_bytes;
     delete c;
     return fail(e == hipErrorOutOfMemory ? KVC_ERR_OOM : KVC_ERR_HIP,
-                "kv_cache_create: device allocation (pools of %zu + %zu bytes) failed: %s", c->k_bytes,
-                c->v_bytes, hipGetErrorString(e));
+                "kv_cache_create: device allocation (pools of %zu + %zu bytes + workspace) failed: %s", kb, vb,
+                hipGetErrorString(e));
   }
   *out = c;
   return KVC_OK;
@@ -159,7 +176,8 @@ int kv_cache_destroy(kvc_handle h) {
   int rc = KVC_OK;
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) rc = hip_fail(e, "kv_cache_destroy: hipDeviceSynchronize");
-  for (void* p : {(void*)h->k_pool, (void*)h->v_pool, (void*)h->scales, (void*)h->amax})
+  for (void* p : {(void*)h->k_pool, (void*)h->v_pool, (void*)h->scales, (void*)h->amax, (void*)h->ws_o,
+                  (void*)h->ws_ml, (void*)h->ws_cnt})
     if (p) (void)hipFree(p);
   delete h;
   return rc;
@@ -253,6 +271,10 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
   a.T = h->T;
   a.H = h->H;
   a.c = scale * 1.4426950408889634f;
+  a.num_cus = h->num_cus;
+  a.ws_o = h->ws_o;
+  a.ws_ml = h->ws_ml;
+  a.ws_cnt = h->ws_cnt;
   if (h->kv_dtype == KVC_KV_FP8) {
     // every chunk has its own scales: one segment per block, the current chunk
     // quantised into the spare slot after the window slots

@@ -24,6 +24,19 @@ struct AttnArgs {
   int H;
   float c;  // softmax scale * log2(e)
   int q_tiles;
+  int q_rows;    // query rows per tile (the last tile of a head may hold fewer)
+  // work split (set by the launcher): n_whole units are computed whole; the
+  // remaining `rest` units are each cut into `slices` key-tile ranges whose
+  // partial results are merged by the slice that finishes last
+  int tiles;     // key tiles of one unit (all segments + the current chunk)
+  int n_whole;
+  int rest;
+  int slices;
+  int grid_whole;  // blocks of the whole-unit part of the grid (multiple of 8)
+  float* ws_o;     // partial O^T of the slices: [piece][wave][register][lane]
+  float* ws_ml;    // partial (max, sum): [piece][wave][2][lane]
+  int* ws_cnt;     // finished slices per split unit: [rest]; zero between calls
+  int num_cus;
   int nseg;
   int32_t seg_row0[kMaxSegments];
   int32_t seg_len[kMaxSegments];
@@ -41,6 +54,11 @@ struct AttnArgs {
 };
 
 // bf16 attention: one workgroup per (head, 128-row query tile), two per CU.
+// Workspace of the split units: bytes of ws_o and ws_ml, and counters, for a
+// device with num_cus compute units.
+size_t attention_ws_o_bytes(int num_cus, int head_dim);
+size_t attention_ws_ml_bytes(int num_cus);
+int attention_ws_counters(int num_cus);
 int launch_attention_bf16(AttnArgs& a, int head_dim, hipStream_t stream);
 
 // Copy K src [H][rows][D] (bf16) into rows [row0, row0 + rows) of a pool [H][pool_rows][D].
