@@ -93,39 +93,6 @@ struct Cfg {
   static_assert(2 * LPW == DS, "the next tile's loads are spread one per k-step of S^T");
 };
 
-// Granule swizzles (see header): rows that share bank groups get different
-// granule positions.  A 256-byte bank window holds one K row for D = 128 and
-// two for D = 64; it holds two V^T tile rows.
-template <int D>
-__device__ __forceinline__ int swz_k(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
-}
-__device__ __forceinline__ int swz_v(int d) { return (d >> 1) & 7; }
-
-constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any resource: reads 0
-
-// Raw buffer resource (range-checked, no stride) of a wave-uniform base and
-// size in bytes, in scalar registers.
-__device__ __forceinline__ u32x4 make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t b = (uint64_t)(uintptr_t)base;
-  const u32x4 r = {(uint32_t)uniform((int)(uint32_t)b), (uint32_t)uniform((int)((b >> 32) & 0xFFFFu)),
-                   (uint32_t)uniform((int)bytes), (uint32_t)kBufFlags};
-  return r;
-}
-
-// 16 bytes per lane from a buffer resource straight into LDS at lds_byte + 16 * lane.
-// Written as inline assembly so the compiler neither waits for it before the
-// kernel's LDS reads (it cannot tell which LDS bytes the load writes) nor keeps
-// those reads from moving past it: the load always writes the buffer that no
-// wave reads until the next barrier.  Completion is awaited explicitly
-// (s_waitcnt vmcnt(0)) before that barrier.  M0 holds the LDS address.
-__device__ __forceinline__ void load_lds16(u32x4 r, uint32_t lds_byte, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds_byte), "v"(voff), "s"(r), "s"(soff)
-               : "m0");
-}
-
 template <int D>
 __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
   using C = Cfg<D>;
@@ -462,7 +429,6 @@ template <int D>
 int launch_cfg(AttnArgs& a, hipStream_t stream) {
   using C = Cfg<D>;
   a.q_tiles = (a.T + C::ROWS - 1) / C::ROWS;
-  a.q_rows = C::ROWS;
   const int units = a.H * a.q_tiles;
   int tiles = (a.T + C::BN - 1) / C::BN;
   for (int s = 0; s < a.nseg; ++s) tiles += (a.seg_len[s] + C::BN - 1) / C::BN;

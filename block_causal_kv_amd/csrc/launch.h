@@ -24,7 +24,6 @@ struct AttnArgs {
   int H;
   float c;  // softmax scale * log2(e)
   int q_tiles;
-  int q_rows;    // query rows per tile (the last tile of a head may hold fewer)
   // work split (set by the launcher): n_whole units are computed whole; the
   // remaining `rest` units are each cut into `slices` key-tile ranges whose
   // partial results are merged by the slice that finishes last
