@@ -19,14 +19,17 @@
 //   of 8 rows, so every 8-key piece of a V^T row is one aligned 16-byte load.
 //
 // Work decomposition
-//   One workgroup = 4 waves = one (head, query tile of 128 rows); each wave owns
-//   32 query rows and keeps their Q in registers.  The workgroup streams the
-//   head's keys in tiles of 64 through two LDS buffers.  Tiles go from global
-//   memory straight into LDS (buffer_load ... lds): no staging registers and no
-//   VALU work for the copy; the loads of tile t+1 are in flight while tile t is
-//   computed, and one barrier per tile hands the buffers over.  Two workgroups
-//   share each CU, so every SIMD holds two waves of independent workgroups and
-//   one wave's MFMAs overlap the other's softmax arithmetic.
+//   One workgroup = 8 waves = one (head, query tile of up to 256 rows; the T
+//   rows of a head are cut into equal tiles); each wave owns 32 query rows and
+//   keeps their Q in registers.  One workgroup per CU: every SIMD holds two of
+//   its waves, and one wave's MFMAs overlap the other's softmax arithmetic.
+//   The workgroup streams the head's keys in tiles of 64 through two LDS
+//   buffers.  Tiles go from global memory straight into LDS (buffer_load ...
+//   lds): no staging registers and no VALU work for the copy; the loads of
+//   tile t+1 are in flight while tile t is computed, and one barrier per tile
+//   hands the buffers over.  Each direct load costs its SIMD issue time, so
+//   sharing one load stream among 256 query rows (rather than two workgroups
+//   of 128 rows loading the same K/V separately) measured a few percent faster.
 //
 // Work split
 //   The (head, query tile) units fill the CUs' workgroup slots in rounds.  When
@@ -74,9 +77,11 @@ namespace {
 
 using namespace dev;
 
+constexpr int kWaves = 8;  // waves per workgroup; one workgroup per CU
+
 template <int D>
 struct Cfg {
-  static constexpr int NW = 4;
+  static constexpr int NW = kWaves;
   static constexpr int NT = NW * 64;         // threads per workgroup
   static constexpr int ROWS = NW * 32;       // query rows per workgroup
   static constexpr int BN = 64;              // keys per tile
@@ -90,11 +95,11 @@ struct Cfg {
   static constexpr int DB = D / 32;          // 32-wide output blocks over the head dim
   static constexpr int KB = BN / 32;         // 32-key blocks per tile
   static_assert(TILE_B % (1024 * NW) == 0, "tile must split into whole 1 KB loads per wave");
-  static_assert(2 * LPW == DS, "the next tile's loads are spread one per k-step of S^T");
+  static_assert(DS % (2 * LPW) == 0, "the next tile's loads are spread evenly over the k-steps of S^T");
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kWaves * 64, 1) void attention_bf16_kernel(AttnArgs a) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::BUF_B];
   __shared__ int s_last;
@@ -135,13 +140,16 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
 
   const int T = a.T;
   const int64_t head_rows = (int64_t)head * T;
-  const int qrow = qtile * C::ROWS + wave * 32 + col;
-  const bool wave_active = qtile * C::ROWS + wave * 32 < T;  // wave-uniform
+  const int row_beg = qtile * a.q_rows;
+  const int row_end = min(T, row_beg + a.q_rows);
+  const int qrow = row_beg + wave * 32 + col;
+  const bool wave_active = row_beg + wave * 32 < row_end;  // wave-uniform
+  const bool row_ok = qrow < row_end;
 
   // ---- Q^T operands in registers
   bf16x8 qreg[C::DS];
   {
-    const bool ok = qrow < T;
+    const bool ok = row_ok;
     const uint16_t* src = a.q + (head_rows + (ok ? qrow : 0)) * D + 8 * hf;
 #pragma unroll
     for (int ds = 0; ds < C::DS; ++ds) {
@@ -265,7 +273,7 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
         const uint4 raw = *(const uint4*)(kl + kaddr[ds] + kb * 32 * C::RB);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw), qreg[ds],
                                                             sacc[kb], 0, 0, 0);
-        if (kb == C::KB - 1 && more) load_one(nplan, ds);  // one load per k-step (2 LPW == DS)
+        if (kb == C::KB - 1 && more && ds % (C::DS / (2 * C::LPW)) == 0) load_one(nplan, ds / (C::DS / (2 * C::LPW)));
       }
     // ---- mask the tail of a partial tile: key of register r = kb*32 + 16*(r/8) + 8*hf + r%8
     if (valid < C::BN) {
@@ -407,7 +415,7 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
 
   // ---- epilogue: O = O^T / l, bf16; lane holds dims db*32 + 8*(r/4) + 4*hf + r%4
   const float l_tot = sum_halves(l_run);
-  if (wave_active && qrow < T) {
+  if (wave_active && row_ok) {
     const float inv = 1.f / l_tot;
     uint16_t* dst = a.o + (head_rows + qrow) * D + 4 * hf;
 #pragma unroll
@@ -422,13 +430,14 @@ __global__ __launch_bounds__(256, 2) void attention_bf16_kernel(AttnArgs a) {
   }
 }
 
-constexpr int kWgPerCu = 2;      // workgroups resident per CU (registers and LDS)
+constexpr int kWgPerCu = 1;      // workgroups resident per CU (registers: 2 waves per SIMD)
 constexpr int kMaxSlices = 8;
 
 template <int D>
 int launch_cfg(AttnArgs& a, hipStream_t stream) {
   using C = Cfg<D>;
   a.q_tiles = (a.T + C::ROWS - 1) / C::ROWS;
+  a.q_rows = (a.T + a.q_tiles - 1) / a.q_tiles;  // equal tiles
   const int units = a.H * a.q_tiles;
   int tiles = (a.T + C::BN - 1) / C::BN;
   for (int s = 0; s < a.nseg; ++s) tiles += (a.seg_len[s] + C::BN - 1) / C::BN;
@@ -467,10 +476,10 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
 // The split pieces number at most 2 x (slots): rest < slots and rest * slices <= 2 * slots.
 int attention_ws_counters(int num_cus) { return kWgPerCu * num_cus; }
 size_t attention_ws_o_bytes(int num_cus, int head_dim) {
-  return (size_t)2 * attention_ws_counters(num_cus) * 4 * (head_dim / 32) * 16 * 64 * sizeof(float);
+  return (size_t)2 * attention_ws_counters(num_cus) * kWaves * (head_dim / 32) * 16 * 64 * sizeof(float);
 }
 size_t attention_ws_ml_bytes(int num_cus) {
-  return (size_t)2 * attention_ws_counters(num_cus) * 4 * 2 * 64 * sizeof(float);
+  return (size_t)2 * attention_ws_counters(num_cus) * kWaves * 2 * 64 * sizeof(float);
 }
 
 int launch_attention_bf16(AttnArgs& a, int head_dim, hipStream_t stream) {

@@ -24,6 +24,7 @@ struct AttnArgs {
   int H;
   float c;  // softmax scale * log2(e)
   int q_tiles;
+  int q_rows;    // query rows per tile (the last tile of a head may hold fewer)
   // work split (set by the launcher): n_whole units are computed whole; the
   // remaining `rest` units are each cut into `slices` key-tile ranges whose
   // partial results are merged by the slice that finishes last
@@ -52,7 +53,7 @@ struct AttnArgs {
   int32_t seg_blk[kMaxSegments];
 };
 
-// bf16 attention: one workgroup per (head, 128-row query tile), two per CU.
+// bf16 attention: one 8-wave workgroup per CU and (head, query tile of up to 256 rows).
 // Workspace of the split units: bytes of ws_o and ws_ml, and counters, for a
 // device with num_cus compute units.
 size_t attention_ws_o_bytes(int num_cus, int head_dim);
