@@ -22,12 +22,18 @@
 //
 // Layout: every segment (condition rows, each resident slot, and the current
 // chunk quantised into the spare slot) is its own segment because scales are
-// per chunk.  K codes [H][rows][D]; V codes transposed [H][D][rows]; tiles of
-// 64 keys, 128 query rows per workgroup (4 waves x 32), two workgroups per CU,
-// double-buffered LDS.  Tile loads are range-checked buffer loads over the
-// whole allocation, so nothing outside it is touched; rows of a partial tile
-// past its segment are masked.  V^T tiles are stored in LDS with each lane
-// half's 32 keys contiguous, in the order its score registers hold them.
+// per chunk.  K codes [H][rows][D]; V codes transposed [H][D][rows]; segment
+// starts and lengths are multiples of 16 rows.  Schedule as in the bf16
+// kernel: one 8-wave workgroup per CU and (head, query tile of up to 256
+// rows), 64-key tiles loaded straight into double-buffered LDS (buffer_load
+// ... lds, spread over the S^T MFMAs), key-slice split of the last round.
+//
+// Key order: K rows are read so that in S^T's accumulator lane half hf holds
+// keys kb*32 + 16*hf + r in register r (16 consecutive keys per 32-key
+// block).  The 32 probabilities of a lane half, packed in register order, are
+// then the keys {16hf .. 16hf+15, 32+16hf .. 32+16hf+15}: exactly 16-byte
+// granules hf and 2+hf of a 64-key V^T tile row, so V^T tiles are plain
+// copies and the PV operand is two 16-byte LDS reads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,17 +49,30 @@ typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 
 template <int D>
 struct F8Cfg {
-  static constexpr int BN = 64;
-  static constexpr int NT = 256;
-  static constexpr int ROWS = 128;
-  static constexpr int KSTR = D + 16;   // bytes per K row in LDS (16 rows -> distinct banks)
-  static constexpr int VTSTR = 64 + 16; // bytes per V^T row in LDS
-  static constexpr int KK = D / 64;     // 64-deep MFMA steps over the head dim
+  static constexpr int NW = 8;
+  static constexpr int NT = NW * 64;
+  static constexpr int ROWS = NW * 32;   // query rows a unit can hold
+  static constexpr int BN = 64;          // keys per tile
+  static constexpr int TILE_K = BN * D;  // bytes of a K code tile (rows of D bytes)
+  static constexpr int TILE_V = D * BN;  // bytes of a V^T code tile (D rows of 64 bytes)
+  static constexpr int BUF_B = TILE_K + TILE_V;
+  static constexpr int KL = TILE_K / 1024;                // 1 KB loads of a K tile
+  static constexpr int LPW = (TILE_K + TILE_V) / 1024 / NW;  // 1 KB loads per wave per tile
+  static constexpr int KK = D / 64;      // 64-deep MFMA steps over the head dim
   static constexpr int DB = D / 32;
-  static constexpr int KPIECES = BN * D / 16 / NT;  // 16-byte K pieces per thread
-  static constexpr int VPIECES = D * BN / 16 / NT;  // 16-byte V^T pieces per thread
-  static_assert(KPIECES >= 1 && VPIECES >= 1, "tile too small for the workgroup");
+  static_assert((TILE_K + TILE_V) % (1024 * NW) == 0 && TILE_K % 1024 == 0, "tiles must split into 1 KB loads");
+  static_assert((KK * 2) % LPW == 0, "the next tile's loads are spread over the S^T steps");
 };
+
+// Granule swizzles (16-byte granules): the 16 lanes reading one granule of the
+// rows krow8(0..15) (K) or of 16 consecutive dim rows (V^T) hit distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_k8(int r) {
+  return D == 128 ? (((r >> 1) & 3) | (((r >> 4) & 1) << 2)) : (((r >> 2) & 1) | (((r >> 4) & 1) << 1));
+}
+__device__ __forceinline__ int swz_v8(int d) { return (d >> 2) & 3; }
+// MFMA row (lane column) -> key within a 32-key block (see header)
+__device__ __forceinline__ int krow8(int col) { return 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3); }
 
 // two floats -> two E4M3 codes in the low 16 bits (round to nearest even)
 __device__ __forceinline__ unsigned pk_fp8(float a, float b) {
@@ -61,35 +80,56 @@ __device__ __forceinline__ unsigned pk_fp8(float a, float b) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attention_fp8_kernel(AttnArgs a) {
+__global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
   using C = F8Cfg<D>;
   constexpr int BN = C::BN;
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[2][BN * C::KSTR];
-  __shared__ __attribute__((aligned(16))) uint8_t v_lds[2][D * C::VTSTR];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::BUF_B];
+  __shared__ int s_last;
+  __shared__ float s_ks[kMaxSegments], s_lv[kMaxSegments];  // per segment: K scale, log2(V scale / vs_ref)
 
-  const int units = a.H * a.q_tiles;
-  const int per_xcd = (units + 7) / 8;
-  const int k_in = blockIdx.x / 8;
-  const int unit = (blockIdx.x % 8) * per_xcd + k_in;
-  if (k_in >= per_xcd || unit >= units) return;
+  int unit, t0 = 0, t1 = a.tiles, piece = -1, ru = 0;
+  {
+    const int b = blockIdx.x;
+    const int xcd = b % 8;
+    if (b < a.grid_whole) {
+      const int per_xcd = (a.n_whole + 7) / 8;
+      const int k_in = b / 8;
+      unit = xcd * per_xcd + k_in;
+      if (k_in >= per_xcd || unit >= a.n_whole) return;
+    } else {
+      const int n_pieces = a.rest * a.slices;
+      const int per_xcd = (n_pieces + 7) / 8;
+      const int k_in = (b - a.grid_whole) / 8;
+      piece = xcd * per_xcd + k_in;
+      if (k_in >= per_xcd || piece >= n_pieces) return;
+      const int slice = piece / a.rest;
+      ru = piece % a.rest;
+      unit = a.n_whole + ru;
+      t0 = (int)((int64_t)slice * a.tiles / a.slices);
+      t1 = (int)((int64_t)(slice + 1) * a.tiles / a.slices);
+    }
+  }
   const int head = unit / a.q_tiles;
   const int qtile = unit % a.q_tiles;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);
   const int hf = lane >> 5;
   const int col = lane & 31;
   const int T = a.T;
   const int64_t head_rows = (int64_t)head * T;
-  const int qrow = qtile * C::ROWS + wave * 32 + col;
-  const bool wave_active = qtile * C::ROWS + wave * 32 < T;
+  const int row_beg = qtile * a.q_rows;
+  const int row_end = min(T, row_beg + a.q_rows);
+  const int qrow = row_beg + wave * 32 + col;
+  const bool wave_active = row_beg + wave * 32 < row_end;  // wave-uniform
+  const bool row_ok = qrow < row_end;
 
   // ---- Q: load this lane's half row (dims kk*64 + 32*hf + 0..31), per-row scale, hi/lo split
   i32x8 qhi[C::KK], qlo[C::KK];
   float sq;
   {
-    const bool ok = qrow < T;
+    const bool ok = row_ok;
     const uint16_t* src = a.q + (head_rows + (ok ? qrow : 0)) * D + 32 * hf;
     float qv[C::KK][32];
 #pragma unroll
@@ -133,13 +173,22 @@ __global__ __launch_bounds__(256, 2) void attention_fp8_kernel(AttnArgs a) {
       qlo[kk] = lv;
     }
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // retire the Q loads (see the bf16 kernel)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // retire the Q loads before the tile loads start
 
   // ---- scales of this head; vs_ref = largest V scale among the segments read
+  // (kept in LDS: a global load inside the tile loop would make the compiler
+  // wait for the tile loads in flight behind it)
   const float* sc_k = a.scales + (int64_t)head * a.scale_head;
   const float* sc_v = a.scales + a.scale_tensor + (int64_t)head * a.scale_head;
   float vs_ref = 0.f;
   for (int s = 0; s < a.nseg; ++s) vs_ref = fmaxf(vs_ref, sc_v[a.seg_blk[uniform(s)]]);
+  if (tid < a.nseg) {
+    const int blk = a.seg_blk[tid];
+    s_ks[tid] = sc_k[blk];
+    s_lv[tid] = __log2f(sc_v[blk] / vs_ref);  // <= 0
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
 
   f32x16 oacc[C::DB];
 #pragma unroll
@@ -149,48 +198,46 @@ __global__ __launch_bounds__(256, 2) void attention_fp8_kernel(AttnArgs a) {
   float m_run = kNegInf, l_run = 0.f;
   const float cq = a.c * sq;  // per-lane part of the score scale
 
-  const int krow = 16 * (col >> 4) + 8 * ((col >> 2) & 1) + 4 * ((col >> 3) & 1) + (col & 3);
-
-  // ---- staging: buffer loads over the whole allocation (out-of-range reads give 0)
-  const __amdgpu_buffer_rsrc_t k_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)a.k8, (short)0, (int)a.k8_bytes, kBufFlags);
-  const __amdgpu_buffer_rsrc_t v_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)a.vt8, (short)0, (int)a.vt8_bytes, kBufFlags);
+  // ---- buffer resources of this head's code rows (range-checked)
   const int64_t prows = a.pool_rows8;
-  uint4 kbuf[C::KPIECES], vbuf[C::VPIECES];
-  auto fetch = [&](Cursor cur) {
-    const int s = uniform(cur.seg);
-    const int r0 = a.seg_row0[s] + cur.off;  // first pool row of the tile
+  const u32x4 rk = make_rsrc(a.k8 + (int64_t)head * prows * D, (uint32_t)(prows * D));
+  const u32x4 rv = make_rsrc(a.vt8 + (int64_t)head * D * prows, (uint32_t)(D * prows));
+
+  // ---- this wave's direct loads (LPW per tile): per-lane offsets and LDS blocks
+  uint32_t voff[C::LPW], ldsoff[C::LPW];
+  int vkey[C::LPW];
+  bool is_k[C::LPW];
 #pragma unroll
-    for (int i = 0; i < C::KPIECES; ++i) {  // K: row = idx / (D/16), 16-byte piece idx % (D/16)
-      const int idx = i * C::NT + tid;
-      const int row = idx / (D / 16), pc = idx % (D / 16);
-      const int off = (int)(((int64_t)head * prows + r0 + row) * D + pc * 16);
-      kbuf[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, off, 0, 0));
+  for (int j = 0; j < C::LPW; ++j) {
+    const int li = wave * C::LPW + j;  // wave-uniform
+    is_k[j] = li < C::KL;
+    if (li < C::KL) {
+      const int r = li * (1024 / D) + lane / (D / 16);
+      const int g = (lane % (D / 16)) ^ swz_k8<D>(r);
+      voff[j] = (uint32_t)(r * D + g * 16);
+      ldsoff[j] = (uint32_t)(li * 1024);
+      vkey[j] = 0;
+    } else {
+      const int b = li - C::KL;
+      const int d = b * 16 + lane / 4;
+      const int g = (lane % 4) ^ swz_v8(d);
+      voff[j] = (uint32_t)((int64_t)d * prows + g * 16);
+      ldsoff[j] = (uint32_t)(C::TILE_K + b * 1024);
+      vkey[j] = 16 * g;
     }
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+
+  // ---- LDS read offsets of the MFMA A operands (buffer 0)
+  const int kr = krow8(col);
+  uint32_t kaddr[C::KK][2], vaddr[2];
 #pragma unroll
-    for (int i = 0; i < C::VPIECES; ++i) {  // V^T: dim row d = idx / 4, keys 16*(idx % 4) + 0..15
-      const int idx = i * C::NT + tid;
-      const int d = idx / 4, q = idx % 4;
-      const int off = (int)(((int64_t)head * D + d) * prows + r0 + 16 * q);
-      vbuf[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(v_rsrc, off, 0, 0));
-    }
-  };
-  auto stash = [&](int buf) {
+  for (int kk = 0; kk < C::KK; ++kk)
 #pragma unroll
-    for (int i = 0; i < C::KPIECES; ++i) {
-      const int idx = i * C::NT + tid;
-      *(uint4*)(&k_lds[buf][(idx / (D / 16)) * C::KSTR + (idx % (D / 16)) * 16]) = kbuf[i];
-    }
+    for (int e = 0; e < 2; ++e) kaddr[kk][e] = (uint32_t)(kr * D + ((kk * 4 + 2 * hf + e) ^ swz_k8<D>(kr)) * 16);
 #pragma unroll
-    for (int i = 0; i < C::VPIECES; ++i) {  // keys 16q+0..7 -> lane half 0, 16q+8..15 -> lane half 1
-      const int idx = i * C::NT + tid;
-      const int d = idx / 4, q = idx % 4;
-      uint8_t* row = &v_lds[buf][d * C::VTSTR];
-      *(uint2*)(row + 8 * q) = make_uint2(vbuf[i].x, vbuf[i].y);
-      *(uint2*)(row + 32 + 8 * q) = make_uint2(vbuf[i].z, vbuf[i].w);
-    }
-  };
+  for (int e = 0; e < 2; ++e) vaddr[e] = (uint32_t)(C::TILE_K + col * 64 + ((2 * e + hf) ^ swz_v8(col)) * 16);
+
   auto seg_len = [&](int s) -> int { return a.seg_len[uniform(s)]; };
   auto advance = [&](Cursor cur) -> Cursor {
     cur.off += BN;
@@ -201,101 +248,193 @@ __global__ __launch_bounds__(256, 2) void attention_fp8_kernel(AttnArgs a) {
     }
     return cur;
   };
+  struct Plan {
+    uint32_t kso, vso, dst;
+    int valid;
+  };
+  auto make_plan = [&](Cursor cur, int buf) -> Plan {
+    Plan p;
+    const int s = uniform(cur.seg);
+    const int row0 = a.seg_row0[s] + cur.off;  // pool row of the tile's first key
+    p.kso = (uint32_t)uniform(row0 * D);
+    p.vso = (uint32_t)uniform(row0);
+    p.dst = (uint32_t)uniform((int)(lds0 + buf * C::BUF_B));
+    p.valid = uniform(min(BN, cur.len - cur.off));
+    return p;
+  };
+  // V^T granules wholly past the segment read as zero (no stale value of a
+  // neighbouring slot meets a zero probability); segment lengths are
+  // multiples of 16, so no granule is partly past it.
+  auto load_one = [&](const Plan& p, int j) {
+    if (is_k[j])
+      load_lds16(rk, p.dst + ldsoff[j], voff[j], p.kso);
+    else
+      load_lds16(rv, p.dst + ldsoff[j], vkey[j] < p.valid ? voff[j] : kOutOfRange, p.vso);
+  };
 
-  Cursor cur = {0, 0, seg_len(0)};
-  fetch(cur);
-  stash(0);
-  __syncthreads();
-  Cursor nxt = advance(cur);
-  if (nxt.seg < a.nseg) fetch(nxt);
-
-  for (int it = 0;; ++it) {
-    const int buf = it & 1;
-    const int valid = min(BN, cur.len - cur.off);
-    if (wave_active) {
-      const int blk = a.seg_blk[uniform(cur.seg)];
-      const float mult = cq * sc_k[blk];          // score = raw * mult (log2 domain)
-      const float lvsr = __log2f(sc_v[blk] / vs_ref);  // <= 0
-      const uint8_t* kl = k_lds[buf];
-      const uint8_t* vl = v_lds[buf];
-      // ---- S^T = Kc . (Q_hi + Q_lo/16)^T
-      f32x16 sacc[2];
+  auto compute = [&](auto buf_tag, const Cursor& cur, const Plan& nplan, bool more) {
+    constexpr int BUF = decltype(buf_tag)::value;
+    if (!wave_active) {
+      if (more)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const uint8_t* p = kl + (kb * 32 + krow) * C::KSTR + kk * 64 + 32 * hf;
-          const uint4 lo = *(const uint4*)p, hi = *(const uint4*)(p + 16);
-          const i32x8 ka = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qhi[kk], sacc[kb], 0, 0, 0, 127, 0, 127);
-          sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qlo[kk], sacc[kb], 0, 0, 0, 127, 0, 123);
-        }
-      if (valid < BN) {  // key of register r = kb*32 + 16*(r/8) + 8*hf + r%8
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7) >= valid) sacc[kb][r] = kNegInf;
-      }
-      // ---- online softmax (base 2, lazy max); P8 carries the V-scale ratio
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = max_halves(mx) * mult;
-      if (__any(mx > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-      const float bias = lvsr - m_run;
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};
-      unsigned pw[8];  // 32 E4M3 probabilities of this lane half, score-register order
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 0], mult, bias));
-          const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 1], mult, bias));
-          const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 2], mult, bias));
-          const float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 3], mult, bias));
-          rs[w] += (e0 + e1) + (e2 + e3);
-          pw[kb * 4 + w] = pk_fp8(e0, e1) | (pk_fp8(e2, e3) << 16);
-        }
-      // the sums carry the factor vs_tile / vs_ref; the denominator must not
-      l_run += ((rs[0] + rs[1]) + (rs[2] + rs[3])) * __builtin_amdgcn_exp2f(-lvsr);
-      const i32x8 pv = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
-      // ---- O^T += Vc^T . P8^T (one 64-key MFMA per 32 dims)
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const uint8_t* p = vl + (db * 32 + col) * C::VTSTR + 32 * hf;
-        const uint4 lo = *(const uint4*)p, hi = *(const uint4*)(p + 16);
-        const i32x8 va = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pv, oacc[db], 0, 0, 0, 127, 0, 127);
-      }
+        for (int j = 0; j < C::LPW; ++j) load_one(nplan, j);
+      return;
     }
-    if (nxt.seg >= a.nseg) break;
-    stash(buf ^ 1);
-    const Cursor nn = advance(nxt);
-    if (nn.seg < a.nseg) fetch(nn);
+    const int valid = min(BN, cur.len - cur.off);
+    const int sg = uniform(cur.seg);
+    const float mult = cq * s_ks[sg];  // score = raw * mult (log2 domain)
+    const float lvsr = s_lv[sg];       // <= 0
+    const uint8_t* tl = lds + BUF * C::BUF_B;
+    // ---- S^T = Kc . (Q_hi + Q_lo/16)^T
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint4 lo = *(const uint4*)(tl + kaddr[kk][0] + kb * 32 * D);
+        const uint4 hi = *(const uint4*)(tl + kaddr[kk][1] + kb * 32 * D);
+        const i32x8 ka = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qhi[kk], sacc[kb], 0, 0, 0, 127, 0, 127);
+        sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qlo[kk], sacc[kb], 0, 0, 0, 127, 0, 123);
+        const int step = kk * 2 + kb;
+        if (more && step % (C::KK * 2 / C::LPW) == 0) load_one(nplan, step / (C::KK * 2 / C::LPW));
+      }
+    if (valid < BN) {  // key of register r = kb*32 + 16*hf + r
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 16 * hf + r >= valid) sacc[kb][r] = kNegInf;
+    }
+    // ---- online softmax (base 2, lazy max); P8 carries the V-scale ratio
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = max_halves(mx) * mult;
+    if (__any(mx > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const float bias = lvsr - m_run;
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    unsigned pw[8];  // 32 E4M3 probabilities of this lane half, register (= key) order
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 0], mult, bias));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 1], mult, bias));
+        const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 2], mult, bias));
+        const float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 3], mult, bias));
+        rs[w] += (e0 + e1) + (e2 + e3);
+        pw[kb * 4 + w] = pk_fp8(e0, e1) | (pk_fp8(e2, e3) << 16);
+      }
+    // the sums carry the factor vs_tile / vs_ref; the denominator must not
+    l_run += ((rs[0] + rs[1]) + (rs[2] + rs[3])) * __builtin_amdgcn_exp2f(-lvsr);
+    const i32x8 pv = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+    // ---- O^T += Vc^T . P8^T (one 64-key MFMA per 32 dims)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const uint4 lo = *(const uint4*)(tl + vaddr[0] + db * 32 * 64);
+      const uint4 hi = *(const uint4*)(tl + vaddr[1] + db * 32 * 64);
+      const i32x8 va = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pv, oacc[db], 0, 0, 0, 127, 0, 127);
+    }
+  };
+
+  // ---- main loop over key tiles [t0, t1), unrolled by two (fixed LDS buffers)
+  Cursor cur;
+  {
+    int rem = t0, sg = 0;
+    for (;;) {  // segment holding tile t0 (t0 < tiles, so this ends)
+      const int len = seg_len(sg);
+      const int nt = (len + BN - 1) / BN;
+      if (rem < nt) {
+        cur = {sg, rem * BN, len};
+        break;
+      }
+      rem -= nt;
+      ++sg;
+    }
+  }
+  int left = uniform(t1 - t0);  // >= 1
+  {
+    const Plan p0 = make_plan(cur, 0);
+#pragma unroll
+    for (int j = 0; j < C::LPW; ++j) load_one(p0, j);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  for (;;) {
+    Cursor nxt = cur;
+    bool more = --left > 0;
+    if (more) nxt = advance(cur);
+    compute(std::integral_constant<int, 0>(), cur, make_plan(nxt, 1), more);
+    if (!more) break;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     cur = nxt;
-    nxt = nn;
+    more = --left > 0;
+    if (more) nxt = advance(cur);
+    compute(std::integral_constant<int, 1>(), cur, make_plan(nxt, 0), more);
+    if (!more) break;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    cur = nxt;
+  }
+
+  // ---- a slice of a split unit: leave the partial result; the last slice merges
+  // (every slice of a unit uses the same vs_ref, so the partials add directly)
+  if (piece >= 0) {
+    constexpr int NR = C::DB * 16;
+    float* po = a.ws_o + (size_t)(piece * C::NW + wave) * NR * 64 + lane;
+    float* pml = a.ws_ml + (size_t)(piece * C::NW + wave) * 2 * 64 + lane;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) po[(db * 16 + r) * 64] = oacc[db][r];
+    pml[0] = m_run;
+    pml[64] = l_run;
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&a.ws_cnt[ru], 1) == a.slices - 1;
+    __syncthreads();
+    if (!s_last) return;
+    __threadfence();
+    const int my_slice = piece / a.rest;
+    for (int j = 0; j < a.slices; ++j) {
+      if (j == my_slice) continue;
+      const size_t pj = (size_t)(j * a.rest + ru) * C::NW + wave;
+      const float* qo = a.ws_o + pj * NR * 64 + lane;
+      const float* qml = a.ws_ml + pj * 2 * 64 + lane;
+      const float mj = qml[0], lj = qml[64];
+      const float mm = fmaxf(m_run, mj);
+      const float a0 = __builtin_amdgcn_exp2f(m_run - mm), a1 = __builtin_amdgcn_exp2f(mj - mm);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a0 + qo[(db * 16 + r) * 64] * a1;
+      l_run = l_run * a0 + lj * a1;
+      m_run = mm;
+    }
+    if (tid == 0) a.ws_cnt[ru] = 0;
   }
 
   // ---- epilogue: O = vs_ref * O^T / l
   const float l_tot = sum_halves(l_run);
-  if (wave_active && qrow < T) {
+  if (wave_active && row_ok) {
     const float f = vs_ref / l_tot;
     uint16_t* dst = a.o + (head_rows + qrow) * D + 4 * hf;
 #pragma unroll
@@ -310,19 +449,50 @@ __global__ __launch_bounds__(256, 2) void attention_fp8_kernel(AttnArgs a) {
   }
 }
 
+constexpr int kMaxSlicesF8 = 8;
+
+template <int D>
+int launch_fp8(AttnArgs& a, hipStream_t stream) {
+  using C = F8Cfg<D>;
+  a.q_tiles = (a.T + C::ROWS - 1) / C::ROWS;
+  a.q_rows = (a.T + a.q_tiles - 1) / a.q_tiles;  // equal tiles
+  const int units = a.H * a.q_tiles;
+  int tiles = 0;
+  for (int s = 0; s < a.nseg; ++s) tiles += (a.seg_len[s] + C::BN - 1) / C::BN;
+  a.tiles = tiles;
+  // split the units of a partly filled last round into key slices (as in the bf16 kernel)
+  const int slots = a.num_cus;  // one workgroup per CU
+  const int rest = units % slots;
+  int slices = 1;
+  double best = rest == 0 ? 0.0 : 1.0;
+  for (int s = 2; s <= kMaxSlicesF8 && s <= tiles && rest * s <= 2 * attention_ws_counters(a.num_cus); ++s) {
+    const double cost = (double)((rest * s + slots - 1) / slots) / s + 0.02 * s;
+    if (cost < best) {
+      best = cost;
+      slices = s;
+    }
+  }
+  if (slices > 1 && a.ws_o != nullptr) {
+    a.rest = rest;
+    a.slices = slices;
+    a.n_whole = units - rest;
+  } else {
+    a.rest = 0;
+    a.slices = 1;
+    a.n_whole = units;
+  }
+  a.grid_whole = 8 * ((a.n_whole + 7) / 8);
+  const int grid = a.grid_whole + 8 * ((a.rest * a.slices + 7) / 8);
+  hipLaunchKernelGGL((attention_fp8_kernel<D>), dim3(grid), dim3(C::NT), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 }  // namespace
 
 int launch_attention_fp8(AttnArgs& a, int head_dim, hipStream_t stream) {
-  a.q_tiles = (a.T + 127) / 128;
-  const int units = a.H * a.q_tiles;
-  const int grid = 8 * ((units + 7) / 8);
-  if (head_dim == 128)
-    hipLaunchKernelGGL(attention_fp8_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
-  else if (head_dim == 64)
-    hipLaunchKernelGGL(attention_fp8_kernel<64>, dim3(grid), dim3(256), 0, stream, a);
-  else
-    return -2;
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  if (head_dim == 128) return launch_fp8<128>(a, stream);
+  if (head_dim == 64) return launch_fp8<64>(a, stream);
+  return -2;
 }
 
 }  // namespace kvc

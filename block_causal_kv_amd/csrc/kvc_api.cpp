@@ -51,7 +51,7 @@ struct kvc_cache {
   uint32_t* amax = nullptr;   // fp8: [2][H] scratch of the quantiser
   int blocks() const { return n_sink + W + 2; }
   int num_cus = 0;
-  float* ws_o = nullptr;   // bf16 attention workspace: partials of split query tiles
+  float* ws_o = nullptr;   // attention workspace: partials of split query tiles
   float* ws_ml = nullptr;
   int* ws_cnt = nullptr;
   kvc::SlotTable table;
@@ -147,10 +147,10 @@ int kv_cache_create(int chunk_tokens, int window_w, int n_sink, int cond_len, in
   if (e == hipSuccess && fp8) e = hipMalloc(&c->amax, sizeof(uint32_t) * 2 * heads);
   if (e == hipSuccess && fp8) e = hipMemset(c->scales, 0, sizeof(float) * 2 * heads * c->blocks());
   const int n_cnt = kvc::attention_ws_counters(c->num_cus);
-  if (e == hipSuccess && !fp8) e = hipMalloc(&c->ws_o, kvc::attention_ws_o_bytes(c->num_cus, head_dim));
-  if (e == hipSuccess && !fp8) e = hipMalloc(&c->ws_ml, kvc::attention_ws_ml_bytes(c->num_cus));
-  if (e == hipSuccess && !fp8) e = hipMalloc(&c->ws_cnt, n_cnt * sizeof(int));
-  if (e == hipSuccess && !fp8) e = hipMemset(c->ws_cnt, 0, n_cnt * sizeof(int));  // counters start at zero
+  if (e == hipSuccess) e = hipMalloc(&c->ws_o, kvc::attention_ws_o_bytes(c->num_cus, head_dim));
+  if (e == hipSuccess) e = hipMalloc(&c->ws_ml, kvc::attention_ws_ml_bytes(c->num_cus));
+  if (e == hipSuccess) e = hipMalloc(&c->ws_cnt, n_cnt * sizeof(int));
+  if (e == hipSuccess) e = hipMemset(c->ws_cnt, 0, n_cnt * sizeof(int));  // counters start at zero
   // the pool starts as zeros: finite values everywhere, zero padding between slots
   if (e == hipSuccess) e = hipMemset(c->k_pool, 0, c->k_bytes);
   if (e == hipSuccess) e = hipMemset(c->v_pool, 0, c->v_bytes);
@@ -296,8 +296,6 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
     ++a.nseg;
     a.k8 = (const uint8_t*)h->k_pool;
     a.vt8 = (const uint8_t*)h->v_pool;
-    a.k8_bytes = (int64_t)h->k_bytes;
-    a.vt8_bytes = (int64_t)h->v_bytes;
     a.pool_rows8 = h->spare_rows;
     a.scales = h->scales;
     a.scale_tensor = h->H * h->blocks();

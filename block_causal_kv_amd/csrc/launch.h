@@ -44,8 +44,6 @@ struct AttnArgs {
   // in the code pools; seg_blk is the segment's scale block.
   const uint8_t* k8;     // K codes [H][pool_rows8][D]
   const uint8_t* vt8;    // V codes, transposed: [H][D][pool_rows8]
-  int64_t k8_bytes;      // allocation sizes (range of the buffer loads)
-  int64_t vt8_bytes;
   int64_t pool_rows8;
   const float* scales;   // [2 (K, V)][H][blocks]
   int scale_tensor;      // H * blocks
