@@ -12,6 +12,8 @@ events around each launch on the launch stream; `cpu_baseline` is the CPU
 oracle on a bounded sample of the same call.
 
     python bench.py [--steps K] [--warmup W] [--config 720p|mid|long] [--no-cpu-baseline]
+    python bench.py --chunks N     (whole-stream form: N chunks in one call)
+    python bench.py --flatness     (300-chunk stream, per-chunk latency)
 """
 from __future__ import annotations
 
@@ -173,6 +175,79 @@ def flatness(args) -> int:
     return 0
 
 
+def stream_flop(spec: synthetic.StreamSpec, n: int) -> float:
+    """Algorithmic FLOP of the whole-stream form over chunks 0..n-1: chunk c
+    sees the condition rows, sinks 0..min(n_sink, lo)-1 and chunks lo..c,
+    lo = max(0, c - W)."""
+    keys = 0
+    for c in range(n):
+        lo = max(0, c - spec.window)
+        keys += spec.cond_len + spec.chunk_tokens * (min(spec.n_sink, lo) + c - lo + 1)
+    return 4.0 * spec.heads * spec.chunk_tokens * keys * spec.head_dim
+
+
+def whole_stream(args) -> int:
+    """Every chunk of an n-chunk stream in one call (the teacher-forcing form of
+    the same mask); each timed step is one such call."""
+    import torch
+    from block_causal_kv_amd import KVCache
+    spec = synthetic.SPECS[args.config]
+    if spec.kv_dtype != "bf16":
+        print("the whole-stream form runs on bf16 K/V only", file=sys.stderr)
+        return 2
+    n = args.chunks
+    H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
+    dev = torch.device("cuda", 0)
+    def dev_bf16(x):
+        return torch.from_numpy(synthetic.bf16_bits(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    sets = []
+    for i in range(min(args.sets, n)):
+        x = synthetic.chunk_inputs(spec, i)
+        sets.append((dev_bf16(x.q[0]), dev_bf16(x.k[0]), dev_bf16(x.v[0])))
+    qkv = [torch.empty((H, n * T, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    for c in range(n):  # chunk c repeats input set c % sets
+        for part in range(3):
+            qkv[part][:, c * T:(c + 1) * T] = sets[c % len(sets)][part]
+    del sets
+    out = torch.empty_like(qkv[0])
+    cache = KVCache(T, spec.window, spec.n_sink, spec.cond_len, H, D)
+    ck, cv = synthetic.cond_inputs(spec)
+    cache.set_condition(dev_bf16(ck), dev_bf16(cv))
+    ws = torch.empty(cache.chunks_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        cache.attention_chunks(*qkv, out=out, workspace=ws, stream=stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        cache.attention_chunks(*qkv, out=out, workspace=ws, stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    fl = stream_flop(spec, n)
+    value = fl * args.steps / elapsed / 1e12
+    achieved = fl / (call_ms * 1e-3) / 1e12
+    rec = {"metric": "whole-stream attention TFLOP/s (every chunk of a %d-chunk stream in one call)" % n,
+           "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1), bf16; 1% of K rows x8)",
+           "config": {"workload": workload_name(spec) + ", %d chunks per call" % n, "chunks": n,
+                      "input_sets": args.sets},
+           "ms_per_chunk": round(elapsed * 1e3 / args.steps / n, 4),
+           "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "algorithmic_flop_per_launch": fl},
+           "cpu_baseline": None}
+    cache.close()
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +259,8 @@ def main() -> int:
     ap.add_argument("--flatness", action="store_true",
                     help="stream the 300-chunk long config from an empty cache and report per-chunk "
                          "latency flatness and device memory instead of the throughput line")
+    ap.add_argument("--chunks", type=int, default=0,
+                    help="time the whole-stream form instead: every chunk of an N-chunk stream in one call")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: attention shards by heads with no exchange, so "
@@ -197,6 +274,8 @@ def main() -> int:
 
     if args.flatness:
         return flatness(args)
+    if args.chunks > 0:
+        return whole_stream(args)
     spec = synthetic.SPECS[args.config]
     H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
     dev = torch.device("cuda", 0)

@@ -116,6 +116,44 @@ class KVCache:
                                               C.c_void_p(_stream_ptr(stream))))
         return out
 
+    def chunks_workspace_bytes(self, n_chunks: int) -> int:
+        n = C.c_size_t()
+        check(self._lib.kvc_chunks_workspace_bytes(self._h, n_chunks, C.byref(n)))
+        return n.value
+
+    def attention_chunks(self, q, k, v, out=None, lse=None, scale: float = 0.0, workspace=None, stream=None):
+        """Block-causal sink + window attention of n consecutive chunks in one call
+        (``sink_window_attention_chunks``): q, k, v are [H][n*T][D] bf16, chunk c
+        at rows c*T .. (c+1)*T - 1.  ``workspace`` (uint8 CUDA tensor) is
+        allocated here if not given.  Returns ``out`` ([H][n*T][D] bf16)."""
+        import torch
+        rows = q.shape[1] if q.dim() == 3 else -1
+        if rows <= 0 or rows % self.T != 0:
+            raise ValueError("q must be [H, n*T, D] with n >= 1 chunks of T = %d rows" % self.T)
+        n = rows // self.T
+        qp = self._check(q, rows, "q")
+        kp = self._check(k, rows, "k")
+        vp = self._check(v, rows, "v")
+        if out is None:
+            out = torch.empty_like(q)
+        op = self._check(out, rows, "out")
+        lp = None
+        if lse is not None:
+            if not lse.is_cuda or lse.dtype != torch.float32 or not lse.is_contiguous() \
+                    or tuple(lse.shape) != (self.H, rows):
+                raise ValueError("lse must be a contiguous float32 CUDA tensor [H, n*T]")
+            lp = C.c_void_p(lse.data_ptr())
+        need = self.chunks_workspace_bytes(n)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous CUDA tensor")
+        wbytes = workspace.numel() * workspace.element_size()
+        check(self._lib.sink_window_attention_chunks(self._h, n, qp, kp, vp, op, lp, C.c_float(scale),
+                                                     C.c_void_p(workspace.data_ptr()), C.c_size_t(wbytes),
+                                                     C.c_void_p(_stream_ptr(stream))))
+        return out
+
 
 class SlotTable:
     """Host-only slot table (``kvc_table_*``): the cache's index logic without a GPU."""

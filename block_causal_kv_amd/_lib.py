@@ -23,6 +23,10 @@ SIGNATURES = {
     "kv_cache_query": (C.c_int, [C.c_void_p, _I64P, _IP, _I64P, C.c_int]),
     "sink_window_attention": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                         C.c_void_p, C.c_float, C.c_void_p]),
+    "sink_window_attention_chunks": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
+                                               C.c_void_p, C.c_void_p, C.c_float, C.c_void_p, C.c_size_t,
+                                               C.c_void_p]),
+    "kvc_chunks_workspace_bytes": (C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_size_t)]),
     "kv_cache_pool_view": (C.c_int, [C.c_void_p, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p),
                                      C.POINTER(C.c_void_p), _I64P, _IP]),
     "kvc_table_create": (C.c_int, [C.c_int, C.c_int, C.POINTER(C.c_void_p)]),

@@ -27,18 +27,21 @@ __global__ __launch_bounds__(256) void rows_copy_kernel(const uint4* __restrict_
   }
 }
 
-// One block: 64 rows of one head (grid: row tiles x H).  Rows past `rows` read
-// as zero, so the last 8-column piece is completed with zeros.
+// One block: 64 rows of one chunk of one head (grid: row tiles x H x chunks).
+// Rows past `rows` read as zero, so the last 8-column piece is completed with
+// zeros.
 template <int D>
 __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t* __restrict__ src,
                                                           uint16_t* __restrict__ vt, int rows, int64_t vt_rows,
-                                                          int col0) {
+                                                          int col0, int col_stride) {
   constexpr int TR = 64;
   constexpr int STR = TR + 8;  // LDS row stride (elements) of the transposed tile
   __shared__ __attribute__((aligned(16))) uint16_t tile[D * STR];
   const int h = blockIdx.y;
+  const int ch = blockIdx.z;
   const int r0 = blockIdx.x * TR;
-  const uint16_t* s = src + ((int64_t)h * rows + r0) * D;
+  const uint16_t* s = src + (((int64_t)h * gridDim.z + ch) * rows + r0) * D;
+  col0 += ch * col_stride;
   constexpr int CH = D / 8;  // 16-byte pieces per input row
   for (int idx = threadIdx.x; idx < TR * CH; idx += blockDim.x) {
     const int r = idx / CH, c8 = idx % CH;
@@ -77,14 +80,14 @@ int launch_rows_copy_bf16(const uint16_t* src, uint16_t* pool, int H, int rows, 
 }
 
 int launch_transpose_v_bf16(const uint16_t* src, uint16_t* vt, int H, int rows, int D, int64_t vt_rows,
-                            int col0, hipStream_t stream) {
-  if (rows <= 0) return 0;
-  if ((col0 & 7) != 0 || (vt_rows & 7) != 0) return -2;
-  const dim3 grid((rows + 63) / 64, H);
+                            int col0, hipStream_t stream, int chunks, int col_stride) {
+  if (rows <= 0 || chunks <= 0) return 0;
+  if ((col0 & 7) != 0 || (vt_rows & 7) != 0 || (col_stride & 7) != 0) return -2;
+  const dim3 grid((rows + 63) / 64, H, chunks);
   if (D == 128)
-    hipLaunchKernelGGL(transpose_v_kernel<128>, grid, dim3(256), 0, stream, src, vt, rows, vt_rows, col0);
+    hipLaunchKernelGGL(transpose_v_kernel<128>, grid, dim3(256), 0, stream, src, vt, rows, vt_rows, col0, col_stride);
   else if (D == 64)
-    hipLaunchKernelGGL(transpose_v_kernel<64>, grid, dim3(256), 0, stream, src, vt, rows, vt_rows, col0);
+    hipLaunchKernelGGL(transpose_v_kernel<64>, grid, dim3(256), 0, stream, src, vt, rows, vt_rows, col0, col_stride);
   else
     return -2;
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -98,7 +98,11 @@ struct Cfg {
   static_assert(DS % (2 * LPW) == 0, "the next tile's loads are spread evenly over the k-steps of S^T");
 };
 
-template <int D>
+// STREAM = false: one call of the cache (segments from the slot table, then
+// the current chunk).  STREAM = true: the whole-stream form, every chunk c of
+// one input attends to the condition rows of the cache and to chunks
+// {0 .. n_sink-1} and {c-W .. c} of the same input (segments derived here).
+template <int D, bool STREAM>
 __global__ __launch_bounds__(kWaves * 64, 1) void attention_bf16_kernel(AttnArgs a) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::BUF_B];
@@ -108,7 +112,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attention_bf16_kernel(AttnArgs
   // a multiple of 8); each XCD gets a contiguous range of items, so the query
   // tiles of one head share that XCD's L2.
   int unit, t0 = 0, t1 = a.tiles, piece = -1, ru = 0;
-  {
+  int chunk = 0;  // stream form: the chunk whose queries this workgroup computes
+  if constexpr (STREAM) {
+    // heaviest chunks first (later chunks see more keys); consecutive items
+    // differ in the head, so the query tiles of a (head, chunk) share an XCD
+    // when H is a multiple of 8
+    const int i = blockIdx.x;
+    if (i >= a.H * a.n_chunks * a.q_tiles) return;
+    const int head_ = i % a.H;
+    const int qt_ = (i / a.H) % a.q_tiles;
+    chunk = a.n_chunks - 1 - i / (a.H * a.q_tiles);
+    unit = head_ * a.q_tiles + qt_;
+  } else {
     const int b = blockIdx.x;
     const int xcd = b % 8;
     if (b < a.grid_whole) {
@@ -129,6 +144,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attention_bf16_kernel(AttnArgs
       t1 = (int)((int64_t)(slice + 1) * a.tiles / a.slices);
     }
   }
+  // stream form: visible chunks [0, ns) and [lo, chunk]; the cond rows come first
+  const int lo = STREAM ? max(0, chunk - a.window) : 0;
+  const int ns = STREAM ? min(a.n_sink, lo) : 0;
+  const int has_cond = STREAM ? (a.cond_len > 0 ? 1 : 0) : 0;
+  if constexpr (STREAM)
+    t1 = has_cond * ((a.cond_len + C::BN - 1) / C::BN) + (ns + chunk - lo + 1) * ((a.T + C::BN - 1) / C::BN);
   const int head = unit / a.q_tiles;
   const int qtile = unit % a.q_tiles;
 
@@ -139,7 +160,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attention_bf16_kernel(AttnArgs
   const int col = lane & 31;  // query column within the wave's 32-row block
 
   const int T = a.T;
-  const int64_t head_rows = (int64_t)head * T;
+  // first row of this head's queries (stream form: of this chunk's queries)
+  const int64_t head_rows = STREAM ? ((int64_t)head * a.n_chunks + chunk) * T : (int64_t)head * T;
   const int row_beg = qtile * a.q_rows;
   const int row_end = min(T, row_beg + a.q_rows);
   const int qrow = row_beg + wave * 32 + col;
@@ -162,13 +184,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attention_bf16_kernel(AttnArgs
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // ---- buffer resources of this head (range-checked: reads past the end give 0)
+  // K: the pool (condition rows, resident slots) or the call's own K (the
+  // current chunk; stream form: every chunk of this head)
   const uint16_t* const kpool_h = a.kpool + (int64_t)head * a.rows_k * D;
-  const uint16_t* const kcur_h = a.kcur + head_rows * D;
-  const uint32_t kpool_bytes = (uint32_t)(a.rows_k * C::RB), kcur_bytes = (uint32_t)(T * C::RB);
-  const u32x4 rv = make_rsrc(a.vt + (int64_t)head * D * a.rows_v, (uint32_t)(D * a.rows_v * 2));
+  const uint16_t* const kcur_h = STREAM ? a.kin + (int64_t)head * a.n_chunks * T * D : a.kcur + head_rows * D;
+  const uint32_t kpool_bytes = (uint32_t)(a.rows_k * C::RB);
+  const uint32_t kcur_bytes = (uint32_t)((STREAM ? a.n_chunks : 1) * T * C::RB);
+  // V^T: the pool (stream form: condition rows only) or the stream form's workspace
+  const u32x4 rv_pool = make_rsrc(a.vt + (int64_t)head * D * a.rows_v, (uint32_t)(D * a.rows_v * 2));
+  const u32x4 rv_ws = STREAM ? make_rsrc(a.vt_ws + (int64_t)head * D * a.ws_rows, (uint32_t)(D * a.ws_rows * 2))
+                             : rv_pool;
 
-  // ---- per-lane offsets of the direct loads (fixed for the call)
-  uint32_t kvo[C::LPW], vvo[C::LPW];
+  // ---- per-lane offsets of the direct loads (fixed for the call): K byte
+  // offset in the tile, V^T dim row and granule
+  uint32_t kvo[C::LPW], vdr[C::LPW];
   int vkey[C::LPW];  // first key (within the tile) of this lane's V^T granule
 #pragma unroll
   for (int j = 0; j < C::LPW; ++j) {
@@ -176,9 +205,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attention_bf16_kernel(AttnArgs
     const int r = b * (1024 / C::RB) + lane / C::GR;
     kvo[j] = (uint32_t)(r * C::RB + ((lane % C::GR) ^ swz_k<D>(r)) * 16);
     const int d = b * (1024 / C::VRB) + lane / 8;
-    const int g = (lane % 8) ^ swz_v(d);
-    vvo[j] = (uint32_t)(d * a.rows_v * 2 + g * 16);
-    vkey[j] = 8 * g;
+    vdr[j] = (uint32_t)d;
+    vkey[j] = 8 * ((lane % 8) ^ swz_v(d));
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
   const uint32_t kblk = (uint32_t)uniform((int)(lds0 + wave * C::LPW * 1024));  // this wave's K blocks, buffer 0
@@ -204,6 +232,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attention_bf16_kernel(AttnArgs
 
   auto seg_len = [&](int s) -> int {
     s = uniform(s);
+    if constexpr (STREAM) return s < has_cond ? a.cond_len : T;
     return s < a.nseg ? a.seg_len[s] : T;
   };
   auto advance = [&](Cursor cur) -> Cursor {
@@ -221,33 +250,46 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attention_bf16_kernel(AttnArgs
   // the MFMAs of the previous tile, so the memory pipeline is fed steadily
   // instead of in a burst that stalls every wave at issue.
   struct Plan {
-    u32x4 rk;
+    u32x4 rk, rv;
     uint32_t kso, vso, kdst, vdst;
     uint32_t vo[C::LPW];
   };
   auto make_plan = [&](Cursor cur, int buf) -> Plan {
     Plan p;
     const int s = uniform(cur.seg);
-    const bool in_pool = s < a.nseg;
     const int valid = min(C::BN, cur.len - cur.off);
-    const int row0 = (in_pool ? a.seg_row0[s] : 0) + cur.off;        // K row of the tile's first key
-    const int vcol0 = (in_pool ? a.seg_row0[s] : a.cur_row0) + cur.off;  // its V^T column
+    bool k_pool, v_pool;
+    int row0, vcol0;  // K row of the tile's first key, its V^T column
+    if constexpr (STREAM) {
+      k_pool = v_pool = s < has_cond;
+      const int i = s - has_cond;
+      const int ch = i < ns ? i : lo + (i - ns);  // the visible chunk of segment s
+      row0 = (k_pool ? 0 : ch * T) + cur.off;
+      vcol0 = (v_pool ? 0 : ch * a.t8) + cur.off;
+    } else {
+      k_pool = s < a.nseg;
+      v_pool = true;
+      row0 = (k_pool ? a.seg_row0[s] : 0) + cur.off;
+      vcol0 = (k_pool ? a.seg_row0[s] : a.cur_row0) + cur.off;
+    }
+    const uint32_t vstride = (uint32_t)uniform((int)(v_pool ? a.rows_v : a.ws_rows) * 2);
     p.kso = (uint32_t)uniform(row0 * C::RB);
     p.vso = (uint32_t)uniform(vcol0 * 2);
-    p.rk = make_rsrc(in_pool ? kpool_h : kcur_h, in_pool ? kpool_bytes : kcur_bytes);
+    p.rk = make_rsrc(k_pool ? kpool_h : kcur_h, k_pool ? kpool_bytes : kcur_bytes);
+    p.rv = v_pool ? rv_pool : rv_ws;
     p.kdst = (uint32_t)uniform((int)(kblk + buf * C::BUF_B));
     p.vdst = (uint32_t)uniform((int)(vblk + buf * C::BUF_B));
     // V^T granules wholly past the segment read as zero, so no stale value of a
     // neighbouring slot meets a zero probability (0 * inf would be NaN).
 #pragma unroll
-    for (int j = 0; j < C::LPW; ++j) p.vo[j] = vkey[j] < valid ? vvo[j] : kOutOfRange;
+    for (int j = 0; j < C::LPW; ++j) p.vo[j] = vkey[j] < valid ? vdr[j] * vstride + 2 * vkey[j] : kOutOfRange;
     return p;
   };
   auto load_one = [&](const Plan& p, int i) {  // i < LPW: K block i, else V^T block i - LPW
     if (i < C::LPW)
       load_lds16(p.rk, p.kdst + i * 1024, kvo[i], p.kso);
     else
-      load_lds16(rv, p.vdst + (i - C::LPW) * 1024, p.vo[i - C::LPW], p.vso);
+      load_lds16(p.rv, p.vdst + (i - C::LPW) * 1024, p.vo[i - C::LPW], p.vso);
   };
 
   // ---- one key tile from LDS buffer BUF
@@ -467,7 +509,20 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
   }
   a.grid_whole = 8 * ((a.n_whole + 7) / 8);
   const int grid = a.grid_whole + 8 * ((a.rest * a.slices + 7) / 8);
-  hipLaunchKernelGGL((attention_bf16_kernel<D>), dim3(grid), dim3(C::NT), 0, stream, a);
+  hipLaunchKernelGGL((attention_bf16_kernel<D, false>), dim3(grid), dim3(C::NT), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+template <int D>
+int launch_chunks(AttnArgs& a, hipStream_t stream) {
+  using C = Cfg<D>;
+  a.q_tiles = (a.T + C::ROWS - 1) / C::ROWS;
+  a.q_rows = (a.T + a.q_tiles - 1) / a.q_tiles;  // equal tiles
+  a.n_whole = a.H * a.n_chunks * a.q_tiles;
+  a.rest = 0;
+  a.slices = 1;
+  const int grid = a.n_whole;
+  hipLaunchKernelGGL((attention_bf16_kernel<D, true>), dim3(grid), dim3(C::NT), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -480,6 +535,12 @@ size_t attention_ws_o_bytes(int num_cus, int head_dim) {
 }
 size_t attention_ws_ml_bytes(int num_cus) {
   return (size_t)2 * attention_ws_counters(num_cus) * kWaves * 2 * 64 * sizeof(float);
+}
+
+int launch_attention_chunks_bf16(AttnArgs& a, int head_dim, hipStream_t stream) {
+  if (head_dim == 128) return launch_chunks<128>(a, stream);
+  if (head_dim == 64) return launch_chunks<64>(a, stream);
+  return -2;
 }
 
 int launch_attention_bf16(AttnArgs& a, int head_dim, hipStream_t stream) {

@@ -323,6 +323,66 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
   return KVC_OK;
 }
 
+int kvc_chunks_workspace_bytes(kvc_handle h, int n_chunks, size_t* out_bytes) {
+  g_last_error.clear();
+  if (!h || !out_bytes) return fail(KVC_ERR_INVALID, "kvc_chunks_workspace_bytes: NULL handle or output");
+  if (n_chunks < 1) return fail(KVC_ERR_INVALID, "kvc_chunks_workspace_bytes: n_chunks = %d < 1", n_chunks);
+  *out_bytes = (size_t)h->H * (size_t)h->D * (size_t)n_chunks * (size_t)kvc::SlotTable::round8(h->T) * 2;
+  return KVC_OK;
+}
+
+int sink_window_attention_chunks(kvc_handle h, int n_chunks, const void* q, const void* k, const void* v,
+                                 void* o, float* lse, float scale, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "sink_window_attention_chunks: handle is NULL");
+  if (h->kv_dtype != KVC_KV_BF16)
+    return fail(KVC_ERR_UNSUPPORTED, "sink_window_attention_chunks: bf16 caches only");
+  if (n_chunks < 1) return fail(KVC_ERR_INVALID, "sink_window_attention_chunks: n_chunks = %d < 1", n_chunks);
+  if (!q || !k || !v || !o || !workspace)
+    return fail(KVC_ERR_INVALID, "sink_window_attention_chunks: NULL q, k, v, o or workspace");
+  const int64_t T8 = kvc::SlotTable::round8(h->T);
+  const int64_t rows = (int64_t)n_chunks * h->T, ws_rows = (int64_t)n_chunks * T8;
+  if (rows * h->D * 2 > INT32_MAX || ws_rows * h->D * 2 > INT32_MAX ||
+      (int64_t)h->H * n_chunks * ((h->T + 255) / 256) > INT32_MAX)
+    return fail(KVC_ERR_INVALID, "sink_window_attention_chunks: %d chunks exceed 32-bit offsets per head",
+                n_chunks);
+  const size_t need = (size_t)h->H * (size_t)h->D * (size_t)ws_rows * 2;
+  if (workspace_bytes < need)
+    return fail(KVC_ERR_INVALID, "sink_window_attention_chunks: workspace of %zu bytes, %zu needed", workspace_bytes,
+                need);
+  if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)h->D);
+  if (!std::isfinite(scale)) return fail(KVC_ERR_INVALID, "sink_window_attention_chunks: scale not finite");
+  kvc::AttnArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = (const uint16_t*)q;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.kpool = (const uint16_t*)h->k_pool;
+  a.vt = (const uint16_t*)h->v_pool;
+  a.rows_k = h->pool_rows;
+  a.rows_v = h->spare_rows;
+  a.T = h->T;
+  a.H = h->H;
+  a.c = scale * 1.4426950408889634f;
+  a.num_cus = h->num_cus;
+  a.n_chunks = n_chunks;
+  a.window = h->W;
+  a.n_sink = h->n_sink;
+  a.cond_len = h->Lc;
+  a.t8 = (int)T8;
+  a.kin = (const uint16_t*)k;
+  a.vt_ws = (const uint16_t*)workspace;
+  a.ws_rows = ws_rows;
+  // V of every chunk, transposed into the workspace (chunk c at column c * T8)
+  if (kvc::launch_transpose_v_bf16((const uint16_t*)v, (uint16_t*)workspace, h->H, h->T, h->D, ws_rows, 0,
+                                   (hipStream_t)stream, n_chunks, (int)T8) != 0)
+    return fail(KVC_ERR_HIP, "sink_window_attention_chunks: transpose launch failed");
+  if (kvc::launch_attention_chunks_bf16(a, h->D, (hipStream_t)stream) != 0)
+    return fail(KVC_ERR_HIP, "sink_window_attention_chunks: launch failed");
+  return KVC_OK;
+}
+
 int kv_cache_pool_view(kvc_handle h, const void** k_pool, const void** v_pool, const float** scales,
                        int64_t* rows, int* blocks) {
   g_last_error.clear();

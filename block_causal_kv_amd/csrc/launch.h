@@ -37,6 +37,15 @@ struct AttnArgs {
   float* ws_ml;    // partial (max, sum): [piece][wave][2][lane]
   int* ws_cnt;     // finished slices per split unit: [rest]; zero between calls
   int num_cus;
+  // whole-stream form (kernel's stream mode): chunks 0..n_chunks-1 of one input
+  int n_chunks;
+  int window;
+  int n_sink;
+  int cond_len;
+  int t8;                // chunk stride of the transposed V workspace (T rounded up to 8)
+  const uint16_t* kin;   // K of all chunks [H][n_chunks * T][D]
+  const uint16_t* vt_ws; // V of all chunks, transposed: [H][D][ws_rows], chunk c at column c * t8
+  int64_t ws_rows;
   int nseg;
   int32_t seg_row0[kMaxSegments];
   int32_t seg_len[kMaxSegments];
@@ -58,16 +67,19 @@ size_t attention_ws_o_bytes(int num_cus, int head_dim);
 size_t attention_ws_ml_bytes(int num_cus);
 int attention_ws_counters(int num_cus);
 int launch_attention_bf16(AttnArgs& a, int head_dim, hipStream_t stream);
+// Whole-stream form: every (head, chunk, query tile) of n_chunks chunks in one launch.
+int launch_attention_chunks_bf16(AttnArgs& a, int head_dim, hipStream_t stream);
 
 // Copy K src [H][rows][D] (bf16) into rows [row0, row0 + rows) of a pool [H][pool_rows][D].
 int launch_rows_copy_bf16(const uint16_t* src, uint16_t* pool, int H, int rows, int D, int64_t pool_rows,
                           int row0, hipStream_t stream);
 
-// Write V src [H][rows][D] (bf16) transposed into columns [col0, col0 + rows) of
-// vt [H][D][vt_rows]; col0 and vt_rows are multiples of 8, and the columns up to
-// the next multiple of 8 are written with zeros.
+// Write V src [H][chunks * rows][D] (bf16) transposed: chunk c's rows go to
+// columns [col0 + c * col_stride, + rows) of vt [H][D][vt_rows].  col0,
+// col_stride and vt_rows are multiples of 8, and each chunk's columns up to the
+// next multiple of 8 are written with zeros.
 int launch_transpose_v_bf16(const uint16_t* src, uint16_t* vt, int H, int rows, int D, int64_t vt_rows,
-                            int col0, hipStream_t stream);
+                            int col0, hipStream_t stream, int chunks = 1, int col_stride = 0);
 
 // fp8 attention (E4M3 K/V codes, per-(head, chunk) scales).
 int launch_attention_fp8(AttnArgs& a, int head_dim, hipStream_t stream);

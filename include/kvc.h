@@ -30,6 +30,7 @@
 #ifndef KVC_H
 #define KVC_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -149,6 +150,35 @@ int kv_cache_query(kvc_handle h, int64_t* next_chunk_id, int* occupancy, int64_t
  */
 int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const void* v_cur,
                           void* o, float* lse, float scale, void* stream);
+
+/*
+ * sink_window_attention_chunks - the same visibility rule for n consecutive
+ * chunks in one call, all from the caller's inputs: the whole-stream
+ * (teacher-forcing) form of the block-causal mask, or a catch-up pass over
+ * several chunks.  Query row r of chunk c = r / T attends to the condition
+ * rows held by the cache (kv_cache_set_condition), to chunks 0 .. n_sink-1
+ * and c-W .. c-1 of the same inputs, and bidirectionally to its own chunk.
+ * Source: tutorial, "From bidirectional editing to a chunk-wise causal
+ * architecture" (the rule over a chunked stream); neurohive.io review,
+ * "Architecture" (figure caption: the mask over the token groups).
+ *
+ *   n_chunks         n >= 1
+ *   q, k, v          bf16 [H][n*T][D]; chunk c occupies rows [c*T, (c+1)*T)
+ *   o                bf16 [H][n*T][D] output; lse float32 [H][n*T] or NULL
+ *   scale            softmax scale; <= 0 selects 1/sqrt(D)
+ *   workspace        device buffer of at least kvc_chunks_workspace_bytes()
+ *                    bytes (V is transposed into it); caller-owned
+ * The cache's slot table and chunk slots are neither read nor changed.  bf16
+ * caches only.  Errors: INVALID (null pointer, n < 1, workspace too small,
+ * sizes beyond 32-bit offsets), UNSUPPORTED (fp8 cache), HIP.
+ */
+int sink_window_attention_chunks(kvc_handle h, int n_chunks, const void* q, const void* k, const void* v,
+                                 void* o, float* lse, float scale, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* Bytes of the workspace sink_window_attention_chunks needs for n_chunks
+ * chunks: H * D * n * round8(T) * 2.  Errors: INVALID. */
+int kvc_chunks_workspace_bytes(kvc_handle h, int n_chunks, size_t* out_bytes);
 
 /*
  * kv_cache_pool_view - device addresses of the pool, for inspection (tests,

@@ -46,6 +46,11 @@ def test_create_rejects_bad_arguments_without_touching_the_gpu():
     assert lib.kv_cache_destroy(None) == _lib.KVC_OK
     assert lib.kv_cache_evict(None, 1, None, None) == _lib.KVC_ERR_INVALID
     assert lib.sink_window_attention(None, None, None, None, None, None, 0.0, None) == _lib.KVC_ERR_INVALID
+    assert lib.sink_window_attention_chunks(None, 2, None, None, None, None, None, 0.0, None, 0,
+                                            None) == _lib.KVC_ERR_INVALID
+    n = C.c_size_t(7)
+    assert lib.kvc_chunks_workspace_bytes(None, 2, C.byref(n)) == _lib.KVC_ERR_INVALID
+    assert n.value == 7
 
 
 @pytest.mark.parametrize("W,S", [(4, 1), (8, 1), (1, 1), (3, 2), (5, 0)])
