@@ -32,13 +32,16 @@
 //   of 128 rows loading the same K/V separately) measured a few percent faster.
 //
 // Work split
-//   The (head, query tile) units fill the CUs' workgroup slots in rounds.  When
-//   the last round would be partly empty, its units are each cut into a few
-//   aligned key-tile ranges (slices) run by separate workgroups: every slice
-//   leaves its unnormalised O^T, running max and partial sums in a workspace,
-//   and the slice that finishes last (device-scope counter, no waiting) merges
-//   them and writes the output.  Slices of one index of the same head's tiles
-//   go to one XCD, so they stream the same K/V through its L2.
+//   Every unit (head, query tile) has the same number of key tiles.  Units
+//   that fill the CUs' workgroup slots in whole rounds run one per workgroup:
+//   the query tiles of a head then stream its K/V in step, and one fetch from
+//   HBM serves them all through the XCD's L2 (each XCD gets a contiguous block
+//   of units).  The units of a last round that is well short of full form a flat
+//   (unit, key tile) space that is cut into one equal contiguous range per
+//   slot: a workgroup computes the pieces of the units its range covers in
+//   turn, and a unit cut by a range boundary is finished by the piece that
+//   ends last, which merges the others' unnormalised O^T, running max and
+//   partial sums from a workspace (device-scope counter, no waiting).
 //
 // LDS tiles (one direct load writes 64 lanes x 16 bytes contiguously)
 //   K tile: 64 rows x D, row r at r * 2D bytes; its 16-byte granule g is stored
@@ -98,6 +101,11 @@ struct Cfg {
   static_assert(DS % (2 * LPW) == 0, "the next tile's loads are spread evenly over the k-steps of S^T");
 };
 
+// Ranges of the flattened (unit, key tile) space: range r starts at
+// floor(r * total / n); range_of(g) is the range holding position g.
+__device__ inline int64_t range_lo(int r, int64_t total, int n) { return (int64_t)r * total / n; }
+__device__ inline int range_of(int64_t g, int64_t total, int n) { return (int)(((g + 1) * n - 1) / total); }
+
 // STREAM = false: one call of the cache (segments from the slot table, then
 // the current chunk).  STREAM = true: the whole-stream form, every chunk c of
 // one input attends to the condition rows of the cache and to chunks
@@ -108,92 +116,40 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attention_bf16_kernel(AttnArgs
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::BUF_B];
   __shared__ int s_last;
 
-  // Work item.  Workgroup b runs on XCD b % 8 (both parts of the grid start on
-  // a multiple of 8); each XCD gets a contiguous range of items, so the query
-  // tiles of one head share that XCD's L2.
-  int unit, t0 = 0, t1 = a.tiles, piece = -1, ru = 0;
-  int chunk = 0;  // stream form: the chunk whose queries this workgroup computes
-  if constexpr (STREAM) {
-    // heaviest chunks first (later chunks see more keys); consecutive items
-    // differ in the head, so the query tiles of a (head, chunk) share an XCD
-    // when H is a multiple of 8
-    const int i = blockIdx.x;
-    if (i >= a.H * a.n_chunks * a.q_tiles) return;
-    const int head_ = i % a.H;
-    const int qt_ = (i / a.H) % a.q_tiles;
-    chunk = a.n_chunks - 1 - i / (a.H * a.q_tiles);
-    unit = head_ * a.q_tiles + qt_;
-  } else {
-    const int b = blockIdx.x;
-    const int xcd = b % 8;
-    if (b < a.grid_whole) {
-      const int per_xcd = (a.n_whole + 7) / 8;
-      const int k_in = b / 8;
-      unit = xcd * per_xcd + k_in;
-      if (k_in >= per_xcd || unit >= a.n_whole) return;
-    } else {
-      const int n_pieces = a.rest * a.slices;
-      const int per_xcd = (n_pieces + 7) / 8;
-      const int k_in = (b - a.grid_whole) / 8;
-      piece = xcd * per_xcd + k_in;
-      if (k_in >= per_xcd || piece >= n_pieces) return;
-      const int slice = piece / a.rest;
-      ru = piece % a.rest;
-      unit = a.n_whole + ru;
-      t0 = (int)((int64_t)slice * a.tiles / a.slices);
-      t1 = (int)((int64_t)(slice + 1) * a.tiles / a.slices);
-    }
-  }
-  // stream form: visible chunks [0, ns) and [lo, chunk]; the cond rows come first
-  const int lo = STREAM ? max(0, chunk - a.window) : 0;
-  const int ns = STREAM ? min(a.n_sink, lo) : 0;
-  const int has_cond = STREAM ? (a.cond_len > 0 ? 1 : 0) : 0;
-  if constexpr (STREAM)
-    t1 = has_cond * ((a.cond_len + C::BN - 1) / C::BN) + (ns + chunk - lo + 1) * ((a.T + C::BN - 1) / C::BN);
-  const int head = unit / a.q_tiles;
-  const int qtile = unit % a.q_tiles;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int hf = lane >> 5;   // lane half
   const int col = lane & 31;  // query column within the wave's 32-row block
-
   const int T = a.T;
-  // first row of this head's queries (stream form: of this chunk's queries)
-  const int64_t head_rows = STREAM ? ((int64_t)head * a.n_chunks + chunk) * T : (int64_t)head * T;
-  const int row_beg = qtile * a.q_rows;
-  const int row_end = min(T, row_beg + a.q_rows);
-  const int qrow = row_beg + wave * 32 + col;
-  const bool wave_active = row_beg + wave * 32 < row_end;  // wave-uniform
-  const bool row_ok = qrow < row_end;
 
-  // ---- Q^T operands in registers
-  bf16x8 qreg[C::DS];
-  {
-    const bool ok = row_ok;
-    const uint16_t* src = a.q + (head_rows + (ok ? qrow : 0)) * D + 8 * hf;
-#pragma unroll
-    for (int ds = 0; ds < C::DS; ++ds) {
-      const uint4 raw = ok ? *(const uint4*)(src + ds * 16) : make_uint4(0, 0, 0, 0);
-      qreg[ds] = __builtin_bit_cast(bf16x8, raw);
+  // ---- work.  Cache call: range r of the (unit, key tile) space, where unit =
+  // (head, query tile) and every unit has a.tiles key tiles.  Workgroup b runs
+  // on XCD b % 8 (the grid is a multiple of 8); each XCD gets a contiguous
+  // block of ranges, so the query tiles of one head share that XCD's L2.
+  // Stream form: one (head, chunk, query tile) per workgroup.
+  int r = 0;
+  int64_t g = 0, g_end = 0;  // positions in the (unit, key tile) space
+  const int64_t base = (int64_t)a.n_whole * a.tiles;  // where the ranges start
+  if constexpr (STREAM) {
+    if (blockIdx.x >= a.H * a.n_chunks * a.q_tiles) return;
+  } else {
+    const int b = blockIdx.x;
+    if (b < a.grid_whole) {  // a whole unit
+      const int per_xcd = (a.n_whole + 7) / 8;
+      const int u = (b % 8) * per_xcd + b / 8;
+      if (b / 8 >= per_xcd || u >= a.n_whole) return;
+      g = (int64_t)u * a.tiles;
+      g_end = g + a.tiles;
+    } else {  // a range of the remaining units
+      const int bb = b - a.grid_whole;
+      const int per_xcd = (a.n_ranges + 7) / 8;
+      r = (bb % 8) * per_xcd + bb / 8;
+      if (bb / 8 >= per_xcd || r >= a.n_ranges) return;
+      g = base + range_lo(r, a.total, a.n_ranges);
+      g_end = base + range_lo(r + 1, a.total, a.n_ranges);
     }
   }
-  // Retire the Q loads now (s_waitcnt vmcnt(0)): otherwise the first use of Q in
-  // the loop waits for every load in flight, the next tile's loads included.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-
-  // ---- buffer resources of this head (range-checked: reads past the end give 0)
-  // K: the pool (condition rows, resident slots) or the call's own K (the
-  // current chunk; stream form: every chunk of this head)
-  const uint16_t* const kpool_h = a.kpool + (int64_t)head * a.rows_k * D;
-  const uint16_t* const kcur_h = STREAM ? a.kin + (int64_t)head * a.n_chunks * T * D : a.kcur + head_rows * D;
-  const uint32_t kpool_bytes = (uint32_t)(a.rows_k * C::RB);
-  const uint32_t kcur_bytes = (uint32_t)((STREAM ? a.n_chunks : 1) * T * C::RB);
-  // V^T: the pool (stream form: condition rows only) or the stream form's workspace
-  const u32x4 rv_pool = make_rsrc(a.vt + (int64_t)head * D * a.rows_v, (uint32_t)(D * a.rows_v * 2));
-  const u32x4 rv_ws = STREAM ? make_rsrc(a.vt_ws + (int64_t)head * D * a.ws_rows, (uint32_t)(D * a.ws_rows * 2))
-                             : rv_pool;
 
   // ---- per-lane offsets of the direct loads (fixed for the call): K byte
   // offset in the tile, V^T dim row and granule
@@ -202,8 +158,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attention_bf16_kernel(AttnArgs
 #pragma unroll
   for (int j = 0; j < C::LPW; ++j) {
     const int b = wave * C::LPW + j;  // 1 KB block of the tile
-    const int r = b * (1024 / C::RB) + lane / C::GR;
-    kvo[j] = (uint32_t)(r * C::RB + ((lane % C::GR) ^ swz_k<D>(r)) * 16);
+    const int rr = b * (1024 / C::RB) + lane / C::GR;
+    kvo[j] = (uint32_t)(rr * C::RB + ((lane % C::GR) ^ swz_k<D>(rr)) * 16);
     const int d = b * (1024 / C::VRB) + lane / 8;
     vdr[j] = (uint32_t)d;
     vkey[j] = 8 * ((lane % 8) ^ swz_v(d));
@@ -222,258 +178,346 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attention_bf16_kernel(AttnArgs
   for (int ks = 0; ks < C::BN / 16; ++ks)
     vaddr[ks] = (uint32_t)(C::TILE_B + col * C::VRB + ((2 * ks + hf) ^ swz_v(col)) * 16);
 
-  f32x16 oacc[C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = kNegInf, l_run = 0.f;
-  const float c = a.c;
-
-  auto seg_len = [&](int s) -> int {
-    s = uniform(s);
-    if constexpr (STREAM) return s < has_cond ? a.cond_len : T;
-    return s < a.nseg ? a.seg_len[s] : T;
-  };
-  auto advance = [&](Cursor cur) -> Cursor {
-    cur.off += C::BN;
-    if (cur.off >= cur.len) {
-      cur.seg += 1;
-      cur.off = 0;
-      cur.len = seg_len(cur.seg);
-    }
-    return cur;
-  };
-
-  // ---- tile producer: this wave's share of the tile's 1 KB blocks (LPW of K,
-  // LPW of V^T) into buffer buf.  The loads are issued one at a time between
-  // the MFMAs of the previous tile, so the memory pipeline is fed steadily
-  // instead of in a burst that stalls every wave at issue.
-  struct Plan {
-    u32x4 rk, rv;
-    uint32_t kso, vso, kdst, vdst;
-    uint32_t vo[C::LPW];
-  };
-  auto make_plan = [&](Cursor cur, int buf) -> Plan {
-    Plan p;
-    const int s = uniform(cur.seg);
-    const int valid = min(C::BN, cur.len - cur.off);
-    bool k_pool, v_pool;
-    int row0, vcol0;  // K row of the tile's first key, its V^T column
+  // ---- the work items of this workgroup: the pieces of the units its range
+  // covers (cache call), or its one unit (stream form)
+  for (int item = 0;; ++item) {
+    int unit, t0, t1;
+    int chunk = 0;  // stream form: the chunk whose queries this workgroup computes
     if constexpr (STREAM) {
-      k_pool = v_pool = s < has_cond;
-      const int i = s - has_cond;
-      const int ch = i < ns ? i : lo + (i - ns);  // the visible chunk of segment s
-      row0 = (k_pool ? 0 : ch * T) + cur.off;
-      vcol0 = (v_pool ? 0 : ch * a.t8) + cur.off;
+      if (item > 0) break;
+      // heaviest chunks first (later chunks see more keys); consecutive items
+      // differ in the head, so the query tiles of a (head, chunk) share an XCD
+      // when H is a multiple of 8
+      const int i = blockIdx.x;
+      const int head_ = i % a.H;
+      const int qt_ = (i / a.H) % a.q_tiles;
+      chunk = a.n_chunks - 1 - i / (a.H * a.q_tiles);
+      unit = head_ * a.q_tiles + qt_;
+      t0 = 0;
+      t1 = 0;  // set below from the visible chunks
     } else {
-      k_pool = s < a.nseg;
-      v_pool = true;
-      row0 = (k_pool ? a.seg_row0[s] : 0) + cur.off;
-      vcol0 = (k_pool ? a.seg_row0[s] : a.cur_row0) + cur.off;
+      if (g >= g_end) break;
+      unit = (int)(g / a.tiles);
+      t0 = (int)(g - (int64_t)unit * a.tiles);
+      t1 = (int)min((int64_t)a.tiles, t0 + (g_end - g));
+      g += t1 - t0;
+      // every wave is done with the previous item's LDS tiles and s_last
+      if (item > 0) __syncthreads();
     }
-    const uint32_t vstride = (uint32_t)uniform((int)(v_pool ? a.rows_v : a.ws_rows) * 2);
-    p.kso = (uint32_t)uniform(row0 * C::RB);
-    p.vso = (uint32_t)uniform(vcol0 * 2);
-    p.rk = make_rsrc(k_pool ? kpool_h : kcur_h, k_pool ? kpool_bytes : kcur_bytes);
-    p.rv = v_pool ? rv_pool : rv_ws;
-    p.kdst = (uint32_t)uniform((int)(kblk + buf * C::BUF_B));
-    p.vdst = (uint32_t)uniform((int)(vblk + buf * C::BUF_B));
-    // V^T granules wholly past the segment read as zero, so no stale value of a
-    // neighbouring slot meets a zero probability (0 * inf would be NaN).
-#pragma unroll
-    for (int j = 0; j < C::LPW; ++j) p.vo[j] = vkey[j] < valid ? vdr[j] * vstride + 2 * vkey[j] : kOutOfRange;
-    return p;
-  };
-  auto load_one = [&](const Plan& p, int i) {  // i < LPW: K block i, else V^T block i - LPW
-    if (i < C::LPW)
-      load_lds16(p.rk, p.kdst + i * 1024, kvo[i], p.kso);
-    else
-      load_lds16(p.rv, p.vdst + (i - C::LPW) * 1024, p.vo[i - C::LPW], p.vso);
-  };
+    // stream form: visible chunks [0, ns) and [lo, chunk]; the cond rows come first
+    const int lo = STREAM ? max(0, chunk - a.window) : 0;
+    const int ns = STREAM ? min(a.n_sink, lo) : 0;
+    const int has_cond = STREAM ? (a.cond_len > 0 ? 1 : 0) : 0;
+    if constexpr (STREAM)
+      t1 = has_cond * ((a.cond_len + C::BN - 1) / C::BN) + (ns + chunk - lo + 1) * ((a.T + C::BN - 1) / C::BN);
+    const int head = unit / a.q_tiles;
+    const int qtile = unit % a.q_tiles;
 
-  // ---- one key tile from LDS buffer BUF
-  auto compute = [&](auto buf_tag, int valid, const Plan& nplan, bool more) {
-    constexpr int BUF = decltype(buf_tag)::value;
-    if (!wave_active) {
-      if (more)
+    // first row of this head's queries (stream form: of this chunk's queries)
+    const int64_t head_rows = STREAM ? ((int64_t)head * a.n_chunks + chunk) * T : (int64_t)head * T;
+    const int row_beg = qtile * a.q_rows;
+    const int row_end = min(T, row_beg + a.q_rows);
+    const int qrow = row_beg + wave * 32 + col;
+    const bool wave_active = row_beg + wave * 32 < row_end;  // wave-uniform
+    const bool row_ok = qrow < row_end;
+
+    // ---- Q^T operands in registers
+    bf16x8 qreg[C::DS];
+    {
+      const bool ok = row_ok;
+      const uint16_t* src = a.q + (head_rows + (ok ? qrow : 0)) * D + 8 * hf;
 #pragma unroll
-        for (int i = 0; i < 2 * C::LPW; ++i) load_one(nplan, i);
-      return;
-    }
-    const uint8_t* kl = lds + BUF * C::BUF_B;
-    // ---- S^T = K . Q^T
-    f32x16 sacc[C::KB];
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
-#pragma unroll
-    for (int ds = 0; ds < C::DS; ++ds)
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        const uint4 raw = *(const uint4*)(kl + kaddr[ds] + kb * 32 * C::RB);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw), qreg[ds],
-                                                            sacc[kb], 0, 0, 0);
-        if (kb == C::KB - 1 && more && ds % (C::DS / (2 * C::LPW)) == 0) load_one(nplan, ds / (C::DS / (2 * C::LPW)));
+      for (int ds = 0; ds < C::DS; ++ds) {
+        const uint4 raw = ok ? *(const uint4*)(src + ds * 16) : make_uint4(0, 0, 0, 0);
+        qreg[ds] = __builtin_bit_cast(bf16x8, raw);
       }
-    // ---- mask the tail of a partial tile: key of register r = kb*32 + 16*(r/8) + 8*hf + r%8
-    if (valid < C::BN) {
+    }
+    // Retire the Q loads now (s_waitcnt vmcnt(0)): otherwise the first use of Q in
+    // the loop waits for every load in flight, the next tile's loads included.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+
+    // ---- buffer resources of this head (range-checked: reads past the end give 0)
+    // K: the pool (condition rows, resident slots) or the call's own K (the
+    // current chunk; stream form: every chunk of this head)
+    const uint16_t* const kpool_h = a.kpool + (int64_t)head * a.rows_k * D;
+    const uint16_t* const kcur_h = STREAM ? a.kin + (int64_t)head * a.n_chunks * T * D : a.kcur + head_rows * D;
+    const uint32_t kpool_bytes = (uint32_t)(a.rows_k * C::RB);
+    const uint32_t kcur_bytes = (uint32_t)((STREAM ? a.n_chunks : 1) * T * C::RB);
+    // V^T: the pool (stream form: condition rows only) or the stream form's workspace
+    const u32x4 rv_pool = make_rsrc(a.vt + (int64_t)head * D * a.rows_v, (uint32_t)(D * a.rows_v * 2));
+    const u32x4 rv_ws = STREAM ? make_rsrc(a.vt_ws + (int64_t)head * D * a.ws_rows, (uint32_t)(D * a.ws_rows * 2))
+                               : rv_pool;
+
+    f32x16 oacc[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) oacc[db][k] = 0.f;
+    float m_run = kNegInf, l_run = 0.f;
+    const float c = a.c;
+
+    auto seg_len = [&](int s) -> int {
+      s = uniform(s);
+      if constexpr (STREAM) return s < has_cond ? a.cond_len : T;
+      return s < a.nseg ? a.seg_len[s] : T;
+    };
+    auto advance = [&](Cursor cur) -> Cursor {
+      cur.off += C::BN;
+      if (cur.off >= cur.len) {
+        cur.seg += 1;
+        cur.off = 0;
+        cur.len = seg_len(cur.seg);
+      }
+      return cur;
+    };
+
+    // ---- tile producer: this wave's share of the tile's 1 KB blocks (LPW of K,
+    // LPW of V^T) into buffer buf.  The loads are issued one at a time between
+    // the MFMAs of the previous tile, so the memory pipeline is fed steadily
+    // instead of in a burst that stalls every wave at issue.
+    struct Plan {
+      u32x4 rk, rv;
+      uint32_t kso, vso, kdst, vdst;
+      uint32_t vo[C::LPW];
+    };
+    auto make_plan = [&](Cursor cur, int buf) -> Plan {
+      Plan p;
+      const int s = uniform(cur.seg);
+      const int valid = min(C::BN, cur.len - cur.off);
+      bool k_pool, v_pool;
+      int row0, vcol0;  // K row of the tile's first key, its V^T column
+      if constexpr (STREAM) {
+        k_pool = v_pool = s < has_cond;
+        const int i = s - has_cond;
+        const int ch = i < ns ? i : lo + (i - ns);  // the visible chunk of segment s
+        row0 = (k_pool ? 0 : ch * T) + cur.off;
+        vcol0 = (v_pool ? 0 : ch * a.t8) + cur.off;
+      } else {
+        k_pool = s < a.nseg;
+        v_pool = true;
+        row0 = (k_pool ? a.seg_row0[s] : 0) + cur.off;
+        vcol0 = (k_pool ? a.seg_row0[s] : a.cur_row0) + cur.off;
+      }
+      const uint32_t vstride = (uint32_t)uniform((int)(v_pool ? a.rows_v : a.ws_rows) * 2);
+      p.kso = (uint32_t)uniform(row0 * C::RB);
+      p.vso = (uint32_t)uniform(vcol0 * 2);
+      p.rk = make_rsrc(k_pool ? kpool_h : kcur_h, k_pool ? kpool_bytes : kcur_bytes);
+      p.rv = v_pool ? rv_pool : rv_ws;
+      p.kdst = (uint32_t)uniform((int)(kblk + buf * C::BUF_B));
+      p.vdst = (uint32_t)uniform((int)(vblk + buf * C::BUF_B));
+      // V^T granules wholly past the segment read as zero, so no stale value of a
+      // neighbouring slot meets a zero probability (0 * inf would be NaN).
+#pragma unroll
+      for (int j = 0; j < C::LPW; ++j) p.vo[j] = vkey[j] < valid ? vdr[j] * vstride + 2 * vkey[j] : kOutOfRange;
+      return p;
+    };
+    auto load_one = [&](const Plan& p, int i) {  // i < LPW: K block i, else V^T block i - LPW
+      if (i < C::LPW)
+        load_lds16(p.rk, p.kdst + i * 1024, kvo[i], p.kso);
+      else
+        load_lds16(p.rv, p.vdst + (i - C::LPW) * 1024, p.vo[i - C::LPW], p.vso);
+    };
+
+    // ---- one key tile from LDS buffer BUF
+    auto compute = [&](auto buf_tag, int valid, const Plan& nplan, bool more) {
+      constexpr int BUF = decltype(buf_tag)::value;
+      if (!wave_active) {
+        if (more)
+#pragma unroll
+          for (int i = 0; i < 2 * C::LPW; ++i) load_one(nplan, i);
+        return;
+      }
+      const uint8_t* kl = lds + BUF * C::BUF_B;
+      // ---- S^T = K . Q^T
+      f32x16 sacc[C::KB];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7) >= valid) sacc[kb][r] = kNegInf;
-    }
-    // ---- online softmax
-    bf16x8 pb[C::KB][2];  // P^T operands: [32-key block][16-key half]
-    float mx = kNegInf;
+        for (int k = 0; k < 16; ++k) sacc[kb][k] = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
+      for (int ds = 0; ds < C::DS; ++ds)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = max_halves(mx) * c;
-    if (__any(mx > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-    // P = exp2(s*c - m) as bf16; the row sum adds the same bf16 values that
-    // enter the PV product.
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        unsigned w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][h2 * 8 + 2 * k], c, -m_run));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][h2 * 8 + 2 * k + 1], c, -m_run));
-          w[k] = pack_bf16(p0, p1);
-          rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[k]),
-                                               __builtin_bit_cast(bf16x2, 0x3f803f80u), rs, false);
+        for (int kb = 0; kb < C::KB; ++kb) {
+          const uint4 raw = *(const uint4*)(kl + kaddr[ds] + kb * 32 * C::RB);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw), qreg[ds],
+                                                              sacc[kb], 0, 0, 0);
+          if (kb == C::KB - 1 && more && ds % (C::DS / (2 * C::LPW)) == 0)
+            load_one(nplan, ds / (C::DS / (2 * C::LPW)));
         }
-        const u32x4 wv = {w[0], w[1], w[2], w[3]};
-        pb[kb][h2] = __builtin_bit_cast(bf16x8, wv);
-      }
-    l_run += rs;
-    // ---- O^T += V^T . P^T
+      // ---- mask the tail of a partial tile: key of register k = kb*32 + 16*(k/8) + 8*hf + k%8
+      if (valid < C::BN) {
 #pragma unroll
-    for (int ks = 0; ks < C::BN / 16; ++ks)
+        for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const uint4 raw = *(const uint4*)(kl + vaddr[ks] + db * 32 * C::VRB);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw),
-                                                            pb[ks >> 1][ks & 1], oacc[db], 0, 0, 0);
+          for (int k = 0; k < 16; ++k)
+            if (kb * 32 + 16 * (k >> 3) + 8 * hf + (k & 7) >= valid) sacc[kb][k] = kNegInf;
       }
-  };
+      // ---- online softmax
+      bf16x8 pb[C::KB][2];  // P^T operands: [32-key block][16-key half]
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) mx = fmaxf(mx, sacc[kb][k]);
+      mx = max_halves(mx) * c;
+      if (__any(mx > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int k = 0; k < 16; ++k) oacc[db][k] *= alpha;
+      }
+      // P = exp2(s*c - m) as bf16; the row sum adds the same bf16 values that
+      // enter the PV product.
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          unsigned w[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][h2 * 8 + 2 * k], c, -m_run));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][h2 * 8 + 2 * k + 1], c, -m_run));
+            w[k] = pack_bf16(p0, p1);
+            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[k]),
+                                                 __builtin_bit_cast(bf16x2, 0x3f803f80u), rs, false);
+          }
+          const u32x4 wv = {w[0], w[1], w[2], w[3]};
+          pb[kb][h2] = __builtin_bit_cast(bf16x8, wv);
+        }
+      l_run += rs;
+      // ---- O^T += V^T . P^T
+#pragma unroll
+      for (int ks = 0; ks < C::BN / 16; ++ks)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const uint4 raw = *(const uint4*)(kl + vaddr[ks] + db * 32 * C::VRB);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw),
+                                                              pb[ks >> 1][ks & 1], oacc[db], 0, 0, 0);
+        }
+    };
 
-  // ---- main loop over key tiles [t0, t1), unrolled by two so each half reads
-  // a fixed buffer.  At the top of a step the tile in buffer `buf` is complete
-  // in LDS (barrier) and the other buffer's previous tile has been read by
-  // every wave (same barrier), so the next tile's loads go there while this
-  // tile is computed.
-  Cursor cur;
-  {
-    int rem = t0, sg = 0;
-    for (;;) {  // segment holding tile t0 (t0 < tiles, so this ends)
-      const int len = seg_len(sg);
-      const int nt = (len + C::BN - 1) / C::BN;
-      if (rem < nt) {
-        cur = {sg, rem * C::BN, len};
-        break;
+    // ---- main loop over key tiles [t0, t1), unrolled by two so each half reads
+    // a fixed buffer.  At the top of a step the tile in buffer `buf` is complete
+    // in LDS (barrier) and the other buffer's previous tile has been read by
+    // every wave (same barrier), so the next tile's loads go there while this
+    // tile is computed.
+    Cursor cur;
+    {
+      int rem = t0, sg = 0;
+      for (;;) {  // segment holding tile t0 (t0 < tiles, so this ends)
+        const int len = seg_len(sg);
+        const int nt = (len + C::BN - 1) / C::BN;
+        if (rem < nt) {
+          cur = {sg, rem * C::BN, len};
+          break;
+        }
+        rem -= nt;
+        ++sg;
       }
-      rem -= nt;
-      ++sg;
     }
-  }
-  int left = uniform(t1 - t0);  // >= 1
-  {
-    const Plan p0 = make_plan(cur, 0);
+    int left = uniform(t1 - t0);  // >= 1
+    {
+      const Plan p0 = make_plan(cur, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * C::LPW; ++i) load_one(p0, i);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-  for (;;) {
-    Cursor nxt = cur;
-    bool more = --left > 0;
-    if (more) nxt = advance(cur);
-    compute(std::integral_constant<int, 0>(), min(C::BN, cur.len - cur.off), make_plan(nxt, 1), more);
-    if (!more) break;
+      for (int i = 0; i < 2 * C::LPW; ++i) load_one(p0, i);
+    }
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    cur = nxt;
-    more = --left > 0;
-    if (more) nxt = advance(cur);
-    compute(std::integral_constant<int, 1>(), min(C::BN, cur.len - cur.off), make_plan(nxt, 0), more);
-    if (!more) break;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    cur = nxt;
-  }
+    for (;;) {
+      Cursor nxt = cur;
+      bool more = --left > 0;
+      if (more) nxt = advance(cur);
+      compute(std::integral_constant<int, 0>(), min(C::BN, cur.len - cur.off), make_plan(nxt, 1), more);
+      if (!more) break;
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      cur = nxt;
+      more = --left > 0;
+      if (more) nxt = advance(cur);
+      compute(std::integral_constant<int, 1>(), min(C::BN, cur.len - cur.off), make_plan(nxt, 0), more);
+      if (!more) break;
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      cur = nxt;
+    }
 
-  // ---- a slice of a split unit: leave the partial result; the last slice merges
-  if (piece >= 0) {
-    constexpr int NR = C::DB * 16;  // O^T registers per lane
-    float* po = a.ws_o + (size_t)(piece * C::NW + wave) * NR * 64 + lane;
-    float* pml = a.ws_ml + (size_t)(piece * C::NW + wave) * 2 * 64 + lane;
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) po[(db * 16 + r) * 64] = oacc[db][r];
-    pml[0] = m_run;
-    pml[64] = l_run;
-    __threadfence();  // publish the partial before counting this slice done
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&a.ws_cnt[ru], 1) == a.slices - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();  // see every other slice's partial
-    const int my_slice = piece / a.rest;
-    for (int j = 0; j < a.slices; ++j) {
-      if (j == my_slice) continue;
-      const size_t pj = (size_t)(j * a.rest + ru) * C::NW + wave;
-      const float* qo = a.ws_o + pj * NR * 64 + lane;
-      const float* qml = a.ws_ml + pj * 2 * 64 + lane;
-      const float mj = qml[0], lj = qml[64];
-      const float mm = fmaxf(m_run, mj);
-      const float a0 = __builtin_amdgcn_exp2f(m_run - mm), a1 = __builtin_amdgcn_exp2f(mj - mm);
+    // ---- a piece of a unit split between ranges: leave the partial result; the
+    // piece that finishes last merges them.  The pieces of unit u are those of
+    // ranges range_of(u0) .. range_of(u0 + tiles - 1); a range holds at most
+    // two pieces (its first item and its last), at workspace slots 2r and 2r+1,
+    // and the unit's counter is that of its last range (the only range that
+    // starts inside it).
+    bool store = true;
+    if (!STREAM && (t0 > 0 || t1 < a.tiles)) {
+      constexpr int NR = C::DB * 16;  // O^T registers per lane
+      const int64_t u0 = (int64_t)unit * a.tiles - base;
+      const int r_first = range_of(u0, a.total, a.n_ranges);
+      const int r_last = range_of(u0 + a.tiles - 1, a.total, a.n_ranges);
+      const int piece = 2 * r + (item == 0 ? 0 : 1);
+      float* po = a.ws_o + (size_t)(piece * C::NW + wave) * NR * 64 + lane;
+      float* pml = a.ws_ml + (size_t)(piece * C::NW + wave) * 2 * 64 + lane;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a0 + qo[(db * 16 + r) * 64] * a1;
-      l_run = l_run * a0 + lj * a1;
-      m_run = mm;
-    }
-    if (tid == 0) a.ws_cnt[ru] = 0;  // ready for the next call
-  }
-
-  // ---- epilogue: O = O^T / l, bf16; lane holds dims db*32 + 8*(r/4) + 4*hf + r%4
-  const float l_tot = sum_halves(l_run);
-  if (wave_active && row_ok) {
-    const float inv = 1.f / l_tot;
-    uint16_t* dst = a.o + (head_rows + qrow) * D + 4 * hf;
+        for (int k = 0; k < 16; ++k) po[(db * 16 + k) * 64] = oacc[db][k];
+      pml[0] = m_run;
+      pml[64] = l_run;
+      __threadfence();  // publish the partial before counting this piece done
+      __syncthreads();
+      if (tid == 0) s_last = atomicAdd(&a.ws_cnt[r_last], 1) == r_last - r_first;
+      __syncthreads();
+      store = s_last;
+      if (store) {
+        __threadfence();  // see every other piece's partial
+        for (int j = r_first; j <= r_last; ++j) {
+          if (j == r) continue;
+          const int slot = (base + range_lo(j, a.total, a.n_ranges)) / a.tiles == unit ? 0 : 1;
+          const size_t pj = (size_t)(2 * j + slot) * C::NW + wave;
+          const float* qo = a.ws_o + pj * NR * 64 + lane;
+          const float* qml = a.ws_ml + pj * 2 * 64 + lane;
+          const float mj = qml[0], lj = qml[64];
+          const float mm = fmaxf(m_run, mj);
+          const float a0 = __builtin_amdgcn_exp2f(m_run - mm), a1 = __builtin_amdgcn_exp2f(mj - mm);
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+          for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t w0 = (uint32_t)f2bf(oacc[db][4 * g + 0] * inv) | ((uint32_t)f2bf(oacc[db][4 * g + 1] * inv) << 16);
-        const uint32_t w1 = (uint32_t)f2bf(oacc[db][4 * g + 2] * inv) | ((uint32_t)f2bf(oacc[db][4 * g + 3] * inv) << 16);
-        *(uint2*)(dst + db * 32 + 8 * g) = make_uint2(w0, w1);
+            for (int k = 0; k < 16; ++k) oacc[db][k] = oacc[db][k] * a0 + qo[(db * 16 + k) * 64] * a1;
+          l_run = l_run * a0 + lj * a1;
+          m_run = mm;
+        }
+        if (tid == 0) a.ws_cnt[r_last] = 0;  // ready for the next call
       }
-    if (a.lse != nullptr && hf == 0) a.lse[head_rows + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+    }
+
+    // ---- epilogue: O = O^T / l, bf16; lane holds dims db*32 + 8*(k/4) + 4*hf + k%4
+    if (store) {
+      const float l_tot = sum_halves(l_run);
+      if (wave_active && row_ok) {
+        const float inv = 1.f / l_tot;
+        uint16_t* dst = a.o + (head_rows + qrow) * D + 4 * hf;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const uint32_t w0 = (uint32_t)f2bf(oacc[db][4 * q4 + 0] * inv) |
+                                ((uint32_t)f2bf(oacc[db][4 * q4 + 1] * inv) << 16);
+            const uint32_t w1 = (uint32_t)f2bf(oacc[db][4 * q4 + 2] * inv) |
+                                ((uint32_t)f2bf(oacc[db][4 * q4 + 3] * inv) << 16);
+            *(uint2*)(dst + db * 32 + 8 * q4) = make_uint2(w0, w1);
+          }
+        if (a.lse != nullptr && hf == 0)
+          a.lse[head_rows + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+      }
+    }
   }
 }
 
 constexpr int kWgPerCu = 1;      // workgroups resident per CU (registers: 2 waves per SIMD)
-constexpr int kMaxSlices = 8;
 
 template <int D>
 int launch_cfg(AttnArgs& a, hipStream_t stream) {
@@ -484,31 +528,27 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
   int tiles = (a.T + C::BN - 1) / C::BN;
   for (int s = 0; s < a.nseg; ++s) tiles += (a.seg_len[s] + C::BN - 1) / C::BN;
   a.tiles = tiles;
-  // Split the units of the last, partly filled round of workgroup slots into
-  // key slices when that shortens it: a round of pieces 1/s as long costs
-  // ceil(rest * s / slots) / s of a whole round (plus a small merge cost).
+  // Whole rounds of units run one unit per workgroup: the query tiles of a head
+  // then stream its K/V in step, so one fetch serves them all through L2.  The
+  // units of a last, partly filled round are instead cut into one equal range
+  // of (unit, key tile) space per workgroup slot (at least one tile per range).
+  // Ranges that do not start on a unit boundary lose that shared stream (the
+  // workgroups of a head sit at different key offsets): measured about 1.35x
+  // slower per tile at 720p-sized K/V.  A last round that is nearly full is
+  // therefore run as whole units.
   const int slots = kWgPerCu * a.num_cus;
-  const int rest = units % slots;
-  int slices = 1;
-  double best = rest == 0 ? 0.0 : 1.0;  // (full rounds need no split)
-  for (int s = 2; s <= kMaxSlices && s <= tiles && rest * s <= attention_ws_counters(a.num_cus) * 2; ++s) {
-    const double cost = (double)((rest * s + slots - 1) / slots) / s + 0.02 * s;
-    if (cost < best) {
-      best = cost;
-      slices = s;
-    }
-  }
-  if (slices > 1 && a.ws_o != nullptr) {
-    a.rest = rest;
-    a.slices = slices;
-    a.n_whole = units - rest;
-  } else {
-    a.rest = 0;
-    a.slices = 1;
-    a.n_whole = units;
-  }
+  int rest = a.ws_o == nullptr ? 0 : units % slots;
+  if (rest > 0 && units > slots && 1.35 * rest / slots + 0.04 >= 1.0) rest = 0;
+  a.n_whole = units - rest;
+  a.total = (int64_t)rest * tiles;
+  if (rest == 0)
+    a.n_ranges = 0;
+  else if (a.total >= slots)
+    a.n_ranges = slots;
+  else
+    a.n_ranges = a.total >= 8 ? (int)(a.total & ~(int64_t)7) : (int)a.total;
   a.grid_whole = 8 * ((a.n_whole + 7) / 8);
-  const int grid = a.grid_whole + 8 * ((a.rest * a.slices + 7) / 8);
+  const int grid = a.grid_whole + 8 * ((a.n_ranges + 7) / 8);
   hipLaunchKernelGGL((attention_bf16_kernel<D, false>), dim3(grid), dim3(C::NT), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
@@ -518,17 +558,14 @@ int launch_chunks(AttnArgs& a, hipStream_t stream) {
   using C = Cfg<D>;
   a.q_tiles = (a.T + C::ROWS - 1) / C::ROWS;
   a.q_rows = (a.T + a.q_tiles - 1) / a.q_tiles;  // equal tiles
-  a.n_whole = a.H * a.n_chunks * a.q_tiles;
-  a.rest = 0;
-  a.slices = 1;
-  const int grid = a.n_whole;
+  const int grid = a.H * a.n_chunks * a.q_tiles;
   hipLaunchKernelGGL((attention_bf16_kernel<D, true>), dim3(grid), dim3(C::NT), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace
 
-// The split pieces number at most 2 x (slots): rest < slots and rest * slices <= 2 * slots.
+// Pieces of split units: at most two per range, one range per workgroup slot.
 int attention_ws_counters(int num_cus) { return kWgPerCu * num_cus; }
 size_t attention_ws_o_bytes(int num_cus, int head_dim) {
   return (size_t)2 * attention_ws_counters(num_cus) * kWaves * (head_dim / 32) * 16 * 64 * sizeof(float);

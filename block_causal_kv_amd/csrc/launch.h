@@ -25,17 +25,23 @@ struct AttnArgs {
   float c;  // softmax scale * log2(e)
   int q_tiles;
   int q_rows;    // query rows per tile (the last tile of a head may hold fewer)
-  // work split (set by the launcher): n_whole units are computed whole; the
-  // remaining `rest` units are each cut into `slices` key-tile ranges whose
-  // partial results are merged by the slice that finishes last
+  // work split (set by the launcher): n_whole units are computed whole, by
+  // grid_whole blocks (a multiple of 8).  fp8 kernel: the remaining `rest`
+  // units are each cut into `slices` key-tile ranges whose partial results are
+  // merged by the slice that finishes last.  bf16 kernel: the (unit, key tile)
+  // space of the remaining units (`total` tiles) is cut into n_ranges equal
+  // contiguous ranges, one per workgroup; a unit that straddles ranges is
+  // computed in pieces merged by the piece finishing last.
   int tiles;     // key tiles of one unit (all segments + the current chunk)
   int n_whole;
   int rest;
   int slices;
-  int grid_whole;  // blocks of the whole-unit part of the grid (multiple of 8)
+  int grid_whole;
+  int n_ranges;
+  int64_t total;
   float* ws_o;     // partial O^T of the slices: [piece][wave][register][lane]
   float* ws_ml;    // partial (max, sum): [piece][wave][2][lane]
-  int* ws_cnt;     // finished slices per split unit: [rest]; zero between calls
+  int* ws_cnt;     // finished pieces per split unit; zero between calls
   int num_cus;
   // whole-stream form (kernel's stream mode): chunks 0..n_chunks-1 of one input
   int n_chunks;
