@@ -37,11 +37,13 @@
 //   the query tiles of a head then stream its K/V in step, and one fetch from
 //   HBM serves them all through the XCD's L2 (each XCD gets a contiguous block
 //   of units).  The units of a last round that is well short of full form a flat
-//   (unit, key tile) space that is cut into one equal contiguous range per
-//   slot: a workgroup computes the pieces of the units its range covers in
-//   turn, and a unit cut by a range boundary is finished by the piece that
-//   ends last, which merges the others' unnormalised O^T, running max and
-//   partial sums from a workspace (device-scope counter, no waiting).
+//   (unit, key tile) space that is cut into equal contiguous ranges: either
+//   each unit into the same s slices (the query tiles of a head stay in step)
+//   or one range per slot (equal work, but unaligned).  A workgroup computes
+//   the pieces of the units its range covers in turn, and a unit cut by a
+//   range boundary is finished by the piece that ends last, which merges the
+//   others' unnormalised O^T, running max and partial sums from a workspace
+//   (device-scope counter, no waiting).
 //
 // LDS tiles (one direct load writes 64 lanes x 16 bytes contiguously)
 //   K tile: 64 rows x D, row r at r * 2D bytes; its 16-byte granule g is stored
@@ -530,23 +532,35 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
   a.tiles = tiles;
   // Whole rounds of units run one unit per workgroup: the query tiles of a head
   // then stream its K/V in step, so one fetch serves them all through L2.  The
-  // units of a last, partly filled round are instead cut into one equal range
-  // of (unit, key tile) space per workgroup slot (at least one tile per range).
-  // Ranges that do not start on a unit boundary lose that shared stream (the
-  // workgroups of a head sit at different key offsets): measured about 1.35x
-  // slower per tile at 720p-sized K/V.  A last round that is nearly full is
-  // therefore run as whole units.
+  // units of the last round are cut into ranges in one of two ways:
+  //  aligned:   n_ranges = rest * s, s = slots / rest: every range is exactly
+  //             1/s of a unit, so the query tiles of a head still stream the
+  //             same K/V in step (slice k of each);
+  //  unaligned: n_ranges = slots: equal work per slot, but ranges start at
+  //             arbitrary key offsets and every workgroup fetches its own K/V
+  //             stream past L2 (measured about 1.35x slower per tile at
+  //             720p-sized K/V).
+  // A last round that is nearly full is run whole instead.  Costs are in units
+  // of one whole-unit round; a split pays a small merge cost per slice.
   const int slots = kWgPerCu * a.num_cus;
   int rest = a.ws_o == nullptr ? 0 : units % slots;
-  if (rest > 0 && units > slots && 1.35 * rest / slots + 0.04 >= 1.0) rest = 0;
+  int n_ranges = 0;
+  if (rest > 0) {
+    const int s = slots / rest;
+    const double aligned = 1.0 / s + (s > 1 ? 0.02 * s : 0.0);
+    const double unaligned = 1.35 * rest / slots + 0.04;
+    const double whole = units > slots ? 1.0 : 1e30;  // (only when other rounds exist)
+    if (whole <= aligned && whole <= unaligned) {
+      rest = 0;
+    } else {
+      const int64_t total = (int64_t)rest * tiles;
+      n_ranges = aligned <= unaligned ? rest * s : slots;
+      if (n_ranges > total) n_ranges = total >= 8 ? (int)(total & ~(int64_t)7) : (int)total;
+    }
+  }
   a.n_whole = units - rest;
   a.total = (int64_t)rest * tiles;
-  if (rest == 0)
-    a.n_ranges = 0;
-  else if (a.total >= slots)
-    a.n_ranges = slots;
-  else
-    a.n_ranges = a.total >= 8 ? (int)(a.total & ~(int64_t)7) : (int)a.total;
+  a.n_ranges = n_ranges;
   a.grid_whole = 8 * ((a.n_whole + 7) / 8);
   const int grid = a.grid_whole + 8 * ((a.n_ranges + 7) / 8);
   hipLaunchKernelGGL((attention_bf16_kernel<D, false>), dim3(grid), dim3(C::NT), 0, stream, a);
