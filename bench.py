@@ -151,6 +151,7 @@ def flatness(args) -> int:
     free0 = torch.cuda.mem_get_info()[0] + torch.cuda.memory_reserved()  # memory outside torch's pool
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(spec.n_chunks)]
+    free_after_first = None
     for c in range(spec.n_chunks):
         q, k, v, kc, vc = sets[c % len(sets)]
         ev[c][0].record(stream)
@@ -158,6 +159,9 @@ def flatness(args) -> int:
             cache.attention(q[st], k[st], v[st], out=out, stream=stream)
         cache.append_chunk(kc, vc, stream=stream)
         ev[c][1].record(stream)
+        if c == 0:  # the runtime sets up per-kernel resources at a kernel's first launch
+            torch.cuda.synchronize()
+            free_after_first = torch.cuda.mem_get_info()[0] + torch.cuda.memory_reserved()
     torch.cuda.synchronize()
     free1 = torch.cuda.mem_get_info()[0] + torch.cuda.memory_reserved()
     ms = [a.elapsed_time(b) for a, b in ev]
@@ -168,6 +172,8 @@ def flatness(args) -> int:
            "dtype": "bf16", "config": {"workload": workload_name(spec), "chunks": spec.n_chunks,
                                        "input_sets": len(sets)},
            "flatness": st, "device_bytes_allocated_during_stream": int(free0 - free1),
+           "device_bytes_allocated_first_chunk_step": int(free0 - free_after_first),
+           "device_bytes_allocated_after_first_chunk_step": int(free_after_first - free1),
            "ms_first_chunks": [round(m, 3) for m in ms[:first_steady + 1]],
            "ms_per_chunk_step_mean_steady": round(float(np.mean(ms[first_steady:])), 4)}
     cache.close()
