@@ -67,11 +67,14 @@ class KVCache:
         return C.c_void_p(t.data_ptr())
 
     def set_condition(self, k, v, stream=None) -> None:
-        if self.Lc == 0:
-            return
-        check(self._lib.kv_cache_set_condition(self._h, self._check(k, self.Lc, "k_cond"),
-                                               self._check(v, self.Lc, "v_cond"),
-                                               C.c_void_p(_stream_ptr(stream))))
+        """Write the condition tokens' K/V ([H][n][D] bf16, n <= Lc; n < Lc
+        replaces the condition by a shorter one, ``kv_cache_set_condition_rows``)."""
+        n = k.shape[1] if k is not None and k.dim() == 3 else self.Lc
+        if n > self.Lc:
+            raise ValueError("condition of %d rows exceeds Lc = %d" % (n, self.Lc))
+        kp = self._check(k, n, "k_cond") if n > 0 else None
+        vp = self._check(v, n, "v_cond") if n > 0 else None
+        check(self._lib.kv_cache_set_condition_rows(self._h, n, kp, vp, C.c_void_p(_stream_ptr(stream))))
 
     def append_chunk(self, k, v, stream=None) -> Tuple[int, int, int]:
         cid, slot, ev = C.c_int64(), C.c_int(), C.c_int64()
@@ -98,22 +101,30 @@ class KVCache:
         return {"next_chunk_id": nxt.value, "occupancy": occ.value, "slots": list(slots)}
 
     def attention(self, q, k_cur, v_cur, out=None, lse=None, scale: float = 0.0, stream=None):
-        """Attention of the next chunk's queries; returns ``out`` ([H][T][D] bf16)."""
+        """Attention of the next chunk's queries; returns ``out`` ([H][n_q][D] bf16).
+
+        q is [H][T][D] for the chunk's own queries (``sink_window_attention``),
+        or [H][n_q][D] for any rows that see the same keys, e.g. the condition
+        tokens' queries (``sink_window_attention_rows``)."""
         import torch
-        qp = self._check(q, self.T, "q")
+        n_q = q.shape[1] if q is not None and q.dim() == 3 else self.T
+        qp = self._check(q, n_q, "q")
         kp = self._check(k_cur, self.T, "k_cur")
         vp = self._check(v_cur, self.T, "v_cur")
         if out is None:
             out = torch.empty_like(q)
-        op = self._check(out, self.T, "out")
+        op = self._check(out, n_q, "out")
         lp = None
         if lse is not None:
             if not lse.is_cuda or lse.dtype != torch.float32 or not lse.is_contiguous() \
-                    or tuple(lse.shape) != (self.H, self.T):
-                raise ValueError("lse must be a contiguous float32 CUDA tensor [H, T]")
+                    or tuple(lse.shape) != (self.H, n_q):
+                raise ValueError("lse must be a contiguous float32 CUDA tensor [H, n_q]")
             lp = C.c_void_p(lse.data_ptr())
-        check(self._lib.sink_window_attention(self._h, qp, kp, vp, op, lp, C.c_float(scale),
-                                              C.c_void_p(_stream_ptr(stream))))
+        st = C.c_void_p(_stream_ptr(stream))
+        if n_q == self.T:
+            check(self._lib.sink_window_attention(self._h, qp, kp, vp, op, lp, C.c_float(scale), st))
+        else:
+            check(self._lib.sink_window_attention_rows(self._h, n_q, qp, kp, vp, op, lp, C.c_float(scale), st))
         return out
 
     def chunks_workspace_bytes(self, n_chunks: int) -> int:

@@ -23,6 +23,9 @@ SIGNATURES = {
     "kv_cache_query": (C.c_int, [C.c_void_p, _I64P, _IP, _I64P, C.c_int]),
     "sink_window_attention": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                         C.c_void_p, C.c_float, C.c_void_p]),
+    "sink_window_attention_rows": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
+                                             C.c_void_p, C.c_void_p, C.c_float, C.c_void_p]),
+    "kv_cache_set_condition_rows": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]),
     "sink_window_attention_chunks": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
                                                C.c_void_p, C.c_void_p, C.c_float, C.c_void_p, C.c_size_t,
                                                C.c_void_p]),

@@ -216,9 +216,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attention_bf16_kernel(AttnArgs
     const int qtile = unit % a.q_tiles;
 
     // first row of this head's queries (stream form: of this chunk's queries)
-    const int64_t head_rows = STREAM ? ((int64_t)head * a.n_chunks + chunk) * T : (int64_t)head * T;
+    const int Tq = STREAM ? T : a.Tq;
+    const int64_t head_rows = STREAM ? ((int64_t)head * a.n_chunks + chunk) * T : (int64_t)head * Tq;
     const int row_beg = qtile * a.q_rows;
-    const int row_end = min(T, row_beg + a.q_rows);
+    const int row_end = min(Tq, row_beg + a.q_rows);
     const int qrow = row_beg + wave * 32 + col;
     const bool wave_active = row_beg + wave * 32 < row_end;  // wave-uniform
     const bool row_ok = qrow < row_end;
@@ -242,7 +243,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attention_bf16_kernel(AttnArgs
     // K: the pool (condition rows, resident slots) or the call's own K (the
     // current chunk; stream form: every chunk of this head)
     const uint16_t* const kpool_h = a.kpool + (int64_t)head * a.rows_k * D;
-    const uint16_t* const kcur_h = STREAM ? a.kin + (int64_t)head * a.n_chunks * T * D : a.kcur + head_rows * D;
+    const uint16_t* const kcur_h =
+        STREAM ? a.kin + (int64_t)head * a.n_chunks * T * D : a.kcur + (int64_t)head * T * D;
     const uint32_t kpool_bytes = (uint32_t)(a.rows_k * C::RB);
     const uint32_t kcur_bytes = (uint32_t)((STREAM ? a.n_chunks : 1) * T * C::RB);
     // V^T: the pool (stream form: condition rows only) or the stream form's workspace
@@ -524,8 +526,8 @@ constexpr int kWgPerCu = 1;      // workgroups resident per CU (registers: 2 wav
 template <int D>
 int launch_cfg(AttnArgs& a, hipStream_t stream) {
   using C = Cfg<D>;
-  a.q_tiles = (a.T + C::ROWS - 1) / C::ROWS;
-  a.q_rows = (a.T + a.q_tiles - 1) / a.q_tiles;  // equal tiles
+  a.q_tiles = (a.Tq + C::ROWS - 1) / C::ROWS;
+  a.q_rows = (a.Tq + a.q_tiles - 1) / a.q_tiles;  // equal tiles
   const int units = a.H * a.q_tiles;
   int tiles = (a.T + C::BN - 1) / C::BN;
   for (int s = 0; s < a.nseg; ++s) tiles += (a.seg_len[s] + C::BN - 1) / C::BN;
@@ -570,6 +572,7 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
 template <int D>
 int launch_chunks(AttnArgs& a, hipStream_t stream) {
   using C = Cfg<D>;
+  a.Tq = a.T;
   a.q_tiles = (a.T + C::ROWS - 1) / C::ROWS;
   a.q_rows = (a.T + a.q_tiles - 1) / a.q_tiles;  // equal tiles
   const int grid = a.H * a.n_chunks * a.q_tiles;

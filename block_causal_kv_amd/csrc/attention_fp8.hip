@@ -117,10 +117,9 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
   const int wave = uniform(tid >> 6);
   const int hf = lane >> 5;
   const int col = lane & 31;
-  const int T = a.T;
-  const int64_t head_rows = (int64_t)head * T;
+  const int64_t head_rows = (int64_t)head * a.Tq;  // first row of this head's queries
   const int row_beg = qtile * a.q_rows;
-  const int row_end = min(T, row_beg + a.q_rows);
+  const int row_end = min(a.Tq, row_beg + a.q_rows);
   const int qrow = row_beg + wave * 32 + col;
   const bool wave_active = row_beg + wave * 32 < row_end;  // wave-uniform
   const bool row_ok = qrow < row_end;
@@ -454,8 +453,8 @@ constexpr int kMaxSlicesF8 = 8;
 template <int D>
 int launch_fp8(AttnArgs& a, hipStream_t stream) {
   using C = F8Cfg<D>;
-  a.q_tiles = (a.T + C::ROWS - 1) / C::ROWS;
-  a.q_rows = (a.T + a.q_tiles - 1) / a.q_tiles;  // equal tiles
+  a.q_tiles = (a.Tq + C::ROWS - 1) / C::ROWS;
+  a.q_rows = (a.Tq + a.q_tiles - 1) / a.q_tiles;  // equal tiles
   const int units = a.H * a.q_tiles;
   int tiles = 0;
   for (int s = 0; s < a.nseg; ++s) tiles += (a.seg_len[s] + C::BN - 1) / C::BN;

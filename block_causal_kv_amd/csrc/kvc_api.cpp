@@ -38,6 +38,7 @@ int hip_fail(hipError_t e, const char* what) {
 
 struct kvc_cache {
   int T, W, n_sink, Lc, H, D, kv_dtype;
+  int cond_rows;  // condition rows in use (<= Lc): the last kv_cache_set_condition_rows
   int device;
   // Pool rows: condition rows [0, Lc), slot s at SlotTable::slot_row0(s, T, Lc)
   // (starts rounded up to multiples of 8), then one spare slot at cur_row0 for
@@ -56,7 +57,7 @@ struct kvc_cache {
   int* ws_cnt = nullptr;
   kvc::SlotTable table;
   kvc_cache(int T_, int W_, int S_, int Lc_, int H_, int D_, int dt)
-      : T(T_), W(W_), n_sink(S_), Lc(Lc_), H(H_), D(D_), kv_dtype(dt), device(0),
+      : T(T_), W(W_), n_sink(S_), Lc(Lc_), H(H_), D(D_), kv_dtype(dt), cond_rows(Lc_), device(0),
         pool_rows(kvc::SlotTable::slot_row0(S_ + W_, T_, Lc_)),
         spare_rows(pool_rows + kvc::SlotTable::round8(T_)), table(W_, S_) {}
 };
@@ -183,19 +184,27 @@ int kv_cache_destroy(kvc_handle h) {
   return rc;
 }
 
+int kv_cache_set_condition_rows(kvc_handle h, int n, const void* k_cond, const void* v_cond, void* stream) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "kv_cache_set_condition_rows: handle is NULL");
+  if (n < 0 || n > h->Lc)
+    return fail(KVC_ERR_INVALID, "kv_cache_set_condition_rows: n = %d outside [0, %d]", n, h->Lc);
+  if (h->kv_dtype == KVC_KV_FP8 && n % 16 != 0)
+    return fail(KVC_ERR_INVALID, "kv_cache_set_condition_rows: fp8 caches need n a multiple of 16 (got %d)", n);
+  if (n > 0 && (!k_cond || !v_cond)) return fail(KVC_ERR_INVALID, "kv_cache_set_condition_rows: NULL K or V");
+  if (n > 0) {
+    const int rc = h->kv_dtype == KVC_KV_FP8 ? quantize_into(h, k_cond, v_cond, n, 0, 0, (hipStream_t)stream)
+                                             : write_bf16(h, k_cond, v_cond, n, 0, (hipStream_t)stream);
+    if (rc != 0) return fail(KVC_ERR_HIP, "kv_cache_set_condition_rows: launch failed");
+  }
+  h->cond_rows = n;
+  return KVC_OK;
+}
+
 int kv_cache_set_condition(kvc_handle h, const void* k_cond, const void* v_cond, void* stream) {
   g_last_error.clear();
   if (!h) return fail(KVC_ERR_INVALID, "kv_cache_set_condition: handle is NULL");
-  if (h->Lc == 0) return KVC_OK;
-  if (!k_cond || !v_cond) return fail(KVC_ERR_INVALID, "kv_cache_set_condition: NULL K or V");
-  if (h->kv_dtype == KVC_KV_FP8) {
-    if (quantize_into(h, k_cond, v_cond, h->Lc, 0, 0, (hipStream_t)stream) != 0)
-      return fail(KVC_ERR_HIP, "kv_cache_set_condition: launch failed");
-    return KVC_OK;
-  }
-  if (write_bf16(h, k_cond, v_cond, h->Lc, 0, (hipStream_t)stream) != 0)
-    return fail(KVC_ERR_HIP, "kv_cache_set_condition: launch failed");
-  return KVC_OK;
+  return kv_cache_set_condition_rows(h, h->Lc, k_cond, v_cond, stream);
 }
 
 int kv_cache_append_chunk(kvc_handle h, const void* k, const void* v, void* stream,
@@ -252,8 +261,17 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
                           void* o, float* lse, float scale, void* stream) {
   g_last_error.clear();
   if (!h) return fail(KVC_ERR_INVALID, "sink_window_attention: handle is NULL");
+  return sink_window_attention_rows(h, h->T, q, k_cur, v_cur, o, lse, scale, stream);
+}
+
+int sink_window_attention_rows(kvc_handle h, int n_q, const void* q, const void* k_cur, const void* v_cur,
+                               void* o, float* lse, float scale, void* stream) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "sink_window_attention: handle is NULL");
   if (!q || !k_cur || !v_cur || !o)
     return fail(KVC_ERR_INVALID, "sink_window_attention: NULL q, k_cur, v_cur or o");
+  if (n_q < 1 || (int64_t)n_q * h->D * 2 > INT32_MAX || (int64_t)h->H * ((n_q + 255) / 256) > INT32_MAX)
+    return fail(KVC_ERR_INVALID, "sink_window_attention: %d query rows (need 1 .. 32-bit offsets)", n_q);
   if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)h->D);
   if (!std::isfinite(scale)) return fail(KVC_ERR_INVALID, "sink_window_attention: scale not finite");
   kvc::AttnArgs a;
@@ -269,6 +287,7 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
   a.rows_v = h->spare_rows;
   a.cur_row0 = (int)h->pool_rows;
   a.T = h->T;
+  a.Tq = n_q;
   a.H = h->H;
   a.c = scale * 1.4426950408889634f;
   a.num_cus = h->num_cus;
@@ -278,7 +297,7 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
   if (h->kv_dtype == KVC_KV_FP8) {
     // every chunk has its own scales: one segment per block, the current chunk
     // quantised into the spare slot after the window slots
-    const std::vector<kvc::Segment> segs = h->table.segments(h->T, h->Lc, false);
+    const std::vector<kvc::Segment> segs = h->table.segments(h->T, h->Lc, false, h->cond_rows);
     if ((int)segs.size() + 1 > kvc::kMaxSegments)
       return fail(KVC_ERR_STATE, "sink_window_attention: %zu segments", segs.size());
     const int n_slots = h->n_sink + h->W;
@@ -306,7 +325,7 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
       return fail(KVC_ERR_HIP, "sink_window_attention: launch failed");
     return KVC_OK;
   }
-  const std::vector<kvc::Segment> segs = h->table.segments(h->T, h->Lc, true);
+  const std::vector<kvc::Segment> segs = h->table.segments(h->T, h->Lc, true, h->cond_rows);
   if ((int)segs.size() > kvc::kMaxSegments)
     return fail(KVC_ERR_STATE, "sink_window_attention: %zu segments", segs.size());
   a.nseg = (int)segs.size();
@@ -369,7 +388,7 @@ int sink_window_attention_chunks(kvc_handle h, int n_chunks, const void* q, cons
   a.n_chunks = n_chunks;
   a.window = h->W;
   a.n_sink = h->n_sink;
-  a.cond_len = h->Lc;
+  a.cond_len = h->cond_rows;
   a.t8 = (int)T8;
   a.kin = (const uint16_t*)k;
   a.vt_ws = (const uint16_t*)workspace;

@@ -10,17 +10,18 @@ constexpr int kMaxSegments = 66;  // condition + up to 64 slots + spare
 // Arguments of one attention call.  Segments are pool row ranges of one head
 // (the same for every head); the current chunk is handled after them.
 struct AttnArgs {
-  const uint16_t* q;     // [H][T][D] bf16
+  const uint16_t* q;     // [H][Tq][D] bf16
   const uint16_t* kcur;  // [H][T][D] bf16 (fp8: codes, see fp8 kernel)
   const uint16_t* vcur;
-  uint16_t* o;           // [H][T][D] bf16
-  float* lse;            // [H][T] or null
+  uint16_t* o;           // [H][Tq][D] bf16
+  float* lse;            // [H][Tq] or null
   const uint16_t* kpool; // bf16 K pool [H][rows_k][D]
   const uint16_t* vt;    // bf16 V pool, transposed: [H][D][rows_v]; the current chunk at cur_row0
   int64_t rows_k;
   int64_t rows_v;
   int cur_row0;
-  int T;
+  int T;         // rows of the current chunk (keys)
+  int Tq;        // query rows per head (T for the chunk's own queries)
   int H;
   float c;  // softmax scale * log2(e)
   int q_tiles;

@@ -49,9 +49,10 @@ void SlotTable::evict(int n, int64_t* ids) {
   }
 }
 
-std::vector<Segment> SlotTable::segments(int chunk_tokens, int cond_len, bool merge) const {
+std::vector<Segment> SlotTable::segments(int chunk_tokens, int cond_len, bool merge, int cond_rows) const {
   std::vector<Segment> out;
-  if (cond_len > 0) out.push_back({0, cond_len, -1});
+  if (cond_rows < 0 || cond_rows > cond_len) cond_rows = cond_len;
+  if (cond_rows > 0) out.push_back({0, cond_rows, -1});
   for (int s = 0; s < n_slots(); ++s) {
     if (slots_[s] < 0) continue;
     const int32_t row0 = slot_row0(s, chunk_tokens, cond_len);

@@ -41,7 +41,10 @@ class SlotTable {
   // Key segments (in pool rows) visible to a query of the next chunk: the
   // condition rows and every occupied slot.  With merge, physically adjacent
   // runs (condition rows and consecutive occupied slots) become one segment.
-  std::vector<Segment> segments(int chunk_tokens, int cond_len, bool merge) const;
+  // cond_rows (<= cond_len, or -1 for all) is the number of condition rows in
+  // use: the layout is fixed by cond_len, a shorter condition leaves the rest
+  // of its block unused.
+  std::vector<Segment> segments(int chunk_tokens, int cond_len, bool merge, int cond_rows = -1) const;
 
   // Pool layout: the condition rows, then one slot of T rows per chunk; the
   // condition block and every slot start on a multiple of 8 rows (the rows in

@@ -93,6 +93,21 @@ int kv_cache_destroy(kvc_handle h);
 int kv_cache_set_condition(kvc_handle h, const void* k_cond, const void* v_cond, void* stream);
 
 /*
+ * kv_cache_set_condition_rows - replace the condition tokens with n rows,
+ * 0 <= n <= Lc (each bf16 [H][n][D]): a new editing instruction mid-stream,
+ * possibly shorter than the first.  Later attention calls see condition rows
+ * [0, n) only; cached chunks are kept.  kv_cache_set_condition is this call
+ * with n = Lc.  Source: neurohive.io review, "Architecture" (condition
+ * tokens are among the groups every chunk attends to); the pages do not
+ * describe changing them during a stream: this reading keeps the video
+ * history and swaps the instruction.
+ * fp8 caches: n a multiple of 16, quantised with a new per-head scale.
+ * Errors: INVALID (n outside [0, Lc], null K/V with n > 0, fp8 n not a
+ * multiple of 16), HIP.
+ */
+int kv_cache_set_condition_rows(kvc_handle h, int n, const void* k_cond, const void* v_cond, void* stream);
+
+/*
  * kv_cache_append_chunk - write the clean K/V of the chunk just generated
  * (each bf16 [H][T][D]) into its slot and update the slot table.
  * Source: tutorial, "Hardware-software co-deployment", bullet "constant KV
@@ -150,6 +165,21 @@ int kv_cache_query(kvc_handle h, int64_t* next_chunk_id, int* occupancy, int64_t
  */
 int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const void* v_cur,
                           void* o, float* lse, float scale, void* stream);
+
+/*
+ * sink_window_attention_rows - as sink_window_attention, for n_q query rows
+ * that all see the key set of the chunk about to be generated: the condition
+ * rows, every resident chunk and the current chunk (k_cur, v_cur [H][T][D]).
+ * For the condition tokens' own queries in a joint-attention layer, or for
+ * [condition queries | chunk queries] in one call.  Source: neurohive.io
+ * review, "Architecture" (condition and video tokens share the MM-DiT's
+ * attention); the pages do not say what condition queries see: this reading
+ * gives them the keys the current chunk sees.
+ *   q, o   bf16 [H][n_q][D];  lse float32 [H][n_q] or NULL
+ * Errors: INVALID (null pointer, n_q < 1, sizes beyond 32-bit offsets), HIP.
+ */
+int sink_window_attention_rows(kvc_handle h, int n_q, const void* q, const void* k_cur, const void* v_cur,
+                               void* o, float* lse, float scale, void* stream);
 
 /*
  * sink_window_attention_chunks - the same visibility rule for n consecutive

@@ -48,6 +48,8 @@ def test_create_rejects_bad_arguments_without_touching_the_gpu():
     assert lib.sink_window_attention(None, None, None, None, None, None, 0.0, None) == _lib.KVC_ERR_INVALID
     assert lib.sink_window_attention_chunks(None, 2, None, None, None, None, None, 0.0, None, 0,
                                             None) == _lib.KVC_ERR_INVALID
+    assert lib.sink_window_attention_rows(None, 5, None, None, None, None, None, 0.0, None) == _lib.KVC_ERR_INVALID
+    assert lib.kv_cache_set_condition_rows(None, 0, None, None, None) == _lib.KVC_ERR_INVALID
     n = C.c_size_t(7)
     assert lib.kvc_chunks_workspace_bytes(None, 2, C.byref(n)) == _lib.KVC_ERR_INVALID
     assert n.value == 7

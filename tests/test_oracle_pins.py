@@ -63,19 +63,22 @@ def test_full_stream_mask_rows_equal_per_chunk_rows():
         assert not blk[:, rows.shape[1]:].any()  # future chunks masked
 
 
-def _gather_form(c, q, k, v, cond_k, cond_v, W, S, scale):
+def _gather_form(c, q, k, v, cond_k, cond_v, W, S, scale, qrows=None):
     """Brute force: list the visible key tokens, then textbook softmax
-    attention with Python loops and math.exp."""
+    attention with Python loops and math.exp.  ``qrows`` ([H, M, D]) replaces
+    chunk c's queries by other rows that see the same keys."""
     H, T, D = q[c].shape
-    out = np.zeros((H, T, D))
+    qq = q[c] if qrows is None else qrows
+    M = qq.shape[1]
+    out = np.zeros((H, M, D))
     hist = [j for j in range(c) if (j < S or c - W <= j)]
     for h in range(H):
         keys = [(cond_k[h, t], cond_v[h, t]) for t in range(cond_k.shape[1])]
         for j in hist:
             keys += [(k[j][h, t], v[j][h, t]) for t in range(T)]
         keys += [(k[c][h, t], v[c][h, t]) for t in range(T)]
-        for i in range(T):
-            scores = [scale * sum(q[c][h, i, d] * kk[d] for d in range(D)) for kk, _ in keys]
+        for i in range(M):
+            scores = [scale * sum(qq[h, i, d] * kk[d] for d in range(D)) for kk, _ in keys]
             mx = max(scores)
             w = [math.exp(s - mx) for s in scores]
             z = sum(w)
@@ -94,6 +97,26 @@ def test_gather_form_equals_mask_form(W, S):
                             cond_k, cond_v, W, S, scale)
         ref = _gather_form(c, q, k, v, cond_k, cond_v, W, S, scale)
         np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("W,S", [(2, 1), (3, 2)])
+def test_extra_query_rows_see_the_chunk_keys(W, S):
+    """Condition-token queries (and any other extra rows) against the gather form
+    over the chunk's visible keys; a shorter condition (a new prompt) is just
+    fewer condition rows."""
+    from oracle.stream import attend_queries
+    n, T, Lc, H, D = 5, 3, 4, 2, 4
+    cond_k, cond_v, q, k, v = _stream(11 + W, n, T, Lc, H, D)
+    rng = np.random.default_rng(5)
+    scale = 0.7
+    for c in range(n):
+        for nc in (Lc, 2):  # full condition, then a shorter replacement
+            ck, cv = cond_k[:, :nc], cond_v[:, :nc]
+            extra = rng.standard_normal((H, 5, D))
+            o, lse = attend_queries(c, extra, k[c], v[c], lambda j: k[j], lambda j: v[j], ck, cv, W, S, scale)
+            ref = _gather_form(c, q, k, v, ck, cv, W, S, scale, qrows=extra)
+            np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+            assert o.shape == (H, 5, D) and lse.shape == (H, 5)
 
 
 def test_masked_attention_matches_torch_sdpa():
