@@ -127,6 +127,45 @@ class KVCache:
             check(self._lib.sink_window_attention_rows(self._h, n_q, qp, kp, vp, op, lp, C.c_float(scale), st))
         return out
 
+    # ---- launch configurations of the attention kernel
+    def configs(self) -> List[Tuple[int, int]]:
+        """(waves per workgroup, workgroups per CU) of each configuration."""
+        n = C.c_int()
+        check(self._lib.kv_cache_config_count(self._h, C.byref(n)))
+        out = []
+        for i in range(n.value):
+            w, g = C.c_int(), C.c_int()
+            check(self._lib.kv_cache_config_info(self._h, i, C.byref(w), C.byref(g)))
+            out.append((w.value, g.value))
+        return out
+
+    @property
+    def config(self) -> int:
+        i = C.c_int()
+        check(self._lib.kv_cache_get_config(self._h, C.byref(i)))
+        return i.value
+
+    @config.setter
+    def config(self, i: int) -> None:
+        check(self._lib.kv_cache_set_config(self._h, int(i)))
+
+    def autotune(self, q, k_cur, v_cur, out=None, reps: int = 5, stream=None) -> Tuple[int, List[float]]:
+        """Time every configuration on this call (kv_cache_autotune) and keep
+        the fastest; returns (chosen id, ms per call of each)."""
+        import torch
+        qp = self._check(q, self.T, "q")
+        kp = self._check(k_cur, self.T, "k_cur")
+        vp = self._check(v_cur, self.T, "v_cur")
+        if out is None:
+            out = torch.empty_like(q)
+        op = self._check(out, self.T, "out")
+        n = len(self.configs())
+        ms = (C.c_float * n)()
+        i = C.c_int()
+        check(self._lib.kv_cache_autotune(self._h, qp, kp, vp, op, int(reps), C.c_void_p(_stream_ptr(stream)),
+                                          C.byref(i), ms))
+        return i.value, [float(x) for x in ms]
+
     def chunks_workspace_bytes(self, n_chunks: int) -> int:
         n = C.c_size_t()
         check(self._lib.kvc_chunks_workspace_bytes(self._h, n_chunks, C.byref(n)))

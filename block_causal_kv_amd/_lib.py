@@ -26,6 +26,12 @@ SIGNATURES = {
     "sink_window_attention_rows": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
                                              C.c_void_p, C.c_void_p, C.c_float, C.c_void_p]),
     "kv_cache_set_condition_rows": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "kv_cache_config_count": (C.c_int, [C.c_void_p, C.POINTER(C.c_int)]),
+    "kv_cache_config_info": (C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_int), C.POINTER(C.c_int)]),
+    "kv_cache_set_config": (C.c_int, [C.c_void_p, C.c_int]),
+    "kv_cache_get_config": (C.c_int, [C.c_void_p, C.POINTER(C.c_int)]),
+    "kv_cache_autotune": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int,
+                                    C.c_void_p, C.POINTER(C.c_int), C.POINTER(C.c_float)]),
     "sink_window_attention_chunks": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
                                                C.c_void_p, C.c_void_p, C.c_float, C.c_void_p, C.c_size_t,
                                                C.c_void_p]),

@@ -82,11 +82,9 @@ namespace {
 
 using namespace dev;
 
-constexpr int kWaves = 8;  // waves per workgroup; one workgroup per CU
-
-template <int D>
+template <int D, int NW_>
 struct Cfg {
-  static constexpr int NW = kWaves;
+  static constexpr int NW = NW_;             // waves per workgroup
   static constexpr int NT = NW * 64;         // threads per workgroup
   static constexpr int ROWS = NW * 32;       // query rows per workgroup
   static constexpr int BN = 64;              // keys per tile
@@ -112,9 +110,9 @@ __device__ inline int range_of(int64_t g, int64_t total, int n) { return (int)((
 // the current chunk).  STREAM = true: the whole-stream form, every chunk c of
 // one input attends to the condition rows of the cache and to chunks
 // {0 .. n_sink-1} and {c-W .. c} of the same input (segments derived here).
-template <int D, bool STREAM>
-__global__ __launch_bounds__(kWaves * 64, 1) void attention_bf16_kernel(AttnArgs a) {
-  using C = Cfg<D>;
+template <int D, int NW, int WGS, bool STREAM>
+__global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a) {
+  using C = Cfg<D, NW>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::BUF_B];
   __shared__ int s_last;
 
@@ -521,11 +519,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attention_bf16_kernel(AttnArgs
   }
 }
 
-constexpr int kWgPerCu = 1;      // workgroups resident per CU (registers: 2 waves per SIMD)
+// Launch configurations: waves per workgroup x workgroups resident per CU
+// (with two waves per SIMD when 8 x 1 or 4 x 2, three when 4 x 3).  The
+// first of each list is the default; which is fastest depends on the head
+// count, chunk length and key count (the round quantisation of units over
+// slots, and how many workgroups share one head's K/V stream), so callers
+// can measure them (kv_cache_autotune).
+struct LaunchCfg {
+  int waves, wgs;
+};
+constexpr LaunchCfg kCfg128[] = {{8, 1}, {4, 2}};
+constexpr LaunchCfg kCfg64[] = {{8, 1}, {4, 2}, {4, 3}};
 
-template <int D>
+template <int D, int NW, int WGS>
 int launch_cfg(AttnArgs& a, hipStream_t stream) {
-  using C = Cfg<D>;
+  using C = Cfg<D, NW>;
   a.q_tiles = (a.Tq + C::ROWS - 1) / C::ROWS;
   a.q_rows = (a.Tq + a.q_tiles - 1) / a.q_tiles;  // equal tiles
   const int units = a.H * a.q_tiles;
@@ -544,7 +552,7 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
   //             720p-sized K/V).
   // A last round that is nearly full is run whole instead.  Costs are in units
   // of one whole-unit round; a split pays a small merge cost per slice.
-  const int slots = kWgPerCu * a.num_cus;
+  const int slots = WGS * a.num_cus;
   int rest = a.ws_o == nullptr ? 0 : units % slots;
   int n_ranges = 0;
   if (rest > 0) {
@@ -565,41 +573,63 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
   a.n_ranges = n_ranges;
   a.grid_whole = 8 * ((a.n_whole + 7) / 8);
   const int grid = a.grid_whole + 8 * ((a.n_ranges + 7) / 8);
-  hipLaunchKernelGGL((attention_bf16_kernel<D, false>), dim3(grid), dim3(C::NT), 0, stream, a);
+  hipLaunchKernelGGL((attention_bf16_kernel<D, NW, WGS, false>), dim3(grid), dim3(C::NT), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-template <int D>
+template <int D, int NW, int WGS>
 int launch_chunks(AttnArgs& a, hipStream_t stream) {
-  using C = Cfg<D>;
+  using C = Cfg<D, NW>;
   a.Tq = a.T;
   a.q_tiles = (a.T + C::ROWS - 1) / C::ROWS;
   a.q_rows = (a.T + a.q_tiles - 1) / a.q_tiles;  // equal tiles
   const int grid = a.H * a.n_chunks * a.q_tiles;
-  hipLaunchKernelGGL((attention_bf16_kernel<D, true>), dim3(grid), dim3(C::NT), 0, stream, a);
+  hipLaunchKernelGGL((attention_bf16_kernel<D, NW, WGS, true>), dim3(grid), dim3(C::NT), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 }  // namespace
 
-// Pieces of split units: at most two per range, one range per workgroup slot.
-int attention_ws_counters(int num_cus) { return kWgPerCu * num_cus; }
+// Pieces of split units: at most two per range, one range per workgroup
+// slot; sized for the largest configuration of the head dim.
+int attention_ws_counters(int num_cus) { return 3 * num_cus; }
 size_t attention_ws_o_bytes(int num_cus, int head_dim) {
-  return (size_t)2 * attention_ws_counters(num_cus) * kWaves * (head_dim / 32) * 16 * 64 * sizeof(float);
+  const int wave_slots = head_dim == 64 ? 12 : 8;  // max waves x workgroups per CU
+  return (size_t)2 * num_cus * wave_slots * (head_dim / 32) * 16 * 64 * sizeof(float);
 }
-size_t attention_ws_ml_bytes(int num_cus) {
-  return (size_t)2 * attention_ws_counters(num_cus) * kWaves * 2 * 64 * sizeof(float);
+size_t attention_ws_ml_bytes(int num_cus) { return (size_t)2 * num_cus * 12 * 2 * 64 * sizeof(float); }
+
+int attention_bf16_configs(int head_dim, int* waves, int* wgs, int cap) {
+  const LaunchCfg* t = head_dim == 128 ? kCfg128 : head_dim == 64 ? kCfg64 : nullptr;
+  const int n = head_dim == 128 ? 2 : head_dim == 64 ? 3 : 0;
+  for (int i = 0; i < n && i < cap; ++i) {
+    if (waves) waves[i] = t[i].waves;
+    if (wgs) wgs[i] = t[i].wgs;
+  }
+  return n;
 }
 
-int launch_attention_chunks_bf16(AttnArgs& a, int head_dim, hipStream_t stream) {
-  if (head_dim == 128) return launch_chunks<128>(a, stream);
-  if (head_dim == 64) return launch_chunks<64>(a, stream);
+int launch_attention_chunks_bf16(AttnArgs& a, int head_dim, int config, hipStream_t stream) {
+  if (head_dim == 128) {
+    if (config == 0) return launch_chunks<128, 8, 1>(a, stream);
+    if (config == 1) return launch_chunks<128, 4, 2>(a, stream);
+  } else if (head_dim == 64) {
+    if (config == 0) return launch_chunks<64, 8, 1>(a, stream);
+    if (config == 1) return launch_chunks<64, 4, 2>(a, stream);
+    if (config == 2) return launch_chunks<64, 4, 3>(a, stream);
+  }
   return -2;
 }
 
-int launch_attention_bf16(AttnArgs& a, int head_dim, hipStream_t stream) {
-  if (head_dim == 128) return launch_cfg<128>(a, stream);
-  if (head_dim == 64) return launch_cfg<64>(a, stream);
+int launch_attention_bf16(AttnArgs& a, int head_dim, int config, hipStream_t stream) {
+  if (head_dim == 128) {
+    if (config == 0) return launch_cfg<128, 8, 1>(a, stream);
+    if (config == 1) return launch_cfg<128, 4, 2>(a, stream);
+  } else if (head_dim == 64) {
+    if (config == 0) return launch_cfg<64, 8, 1>(a, stream);
+    if (config == 1) return launch_cfg<64, 4, 2>(a, stream);
+    if (config == 2) return launch_cfg<64, 4, 3>(a, stream);
+  }
   return -2;
 }
 

@@ -464,7 +464,8 @@ int launch_fp8(AttnArgs& a, hipStream_t stream) {
   const int rest = units % slots;
   int slices = 1;
   double best = rest == 0 ? 0.0 : 1.0;
-  for (int s = 2; s <= kMaxSlicesF8 && s <= tiles && rest * s <= 2 * attention_ws_counters(a.num_cus); ++s) {
+  // (the workspace holds 2 x num_cus pieces of 8 waves)
+  for (int s = 2; s <= kMaxSlicesF8 && s <= tiles && rest * s <= 2 * slots; ++s) {
     const double cost = (double)((rest * s + slots - 1) / slots) / s + 0.02 * s;
     if (cost < best) {
       best = cost;

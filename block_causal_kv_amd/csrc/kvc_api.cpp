@@ -55,6 +55,7 @@ struct kvc_cache {
   float* ws_o = nullptr;   // attention workspace: partials of split query tiles
   float* ws_ml = nullptr;
   int* ws_cnt = nullptr;
+  int config = 0;  // bf16 attention launch configuration (kv_cache_set_config)
   kvc::SlotTable table;
   kvc_cache(int T_, int W_, int S_, int Lc_, int H_, int D_, int dt)
       : T(T_), W(W_), n_sink(S_), Lc(Lc_), H(H_), D(D_), kv_dtype(dt), cond_rows(Lc_), device(0),
@@ -337,8 +338,99 @@ int sink_window_attention_rows(kvc_handle h, int n_q, const void* q, const void*
   if (kvc::launch_transpose_v_bf16((const uint16_t*)v_cur, (uint16_t*)h->v_pool, h->H, h->T, h->D, h->spare_rows,
                                    (int)h->pool_rows, (hipStream_t)stream) != 0)
     return fail(KVC_ERR_HIP, "sink_window_attention: transpose launch failed");
-  if (kvc::launch_attention_bf16(a, h->D, (hipStream_t)stream) != 0)
+  if (kvc::launch_attention_bf16(a, h->D, h->config, (hipStream_t)stream) != 0)
     return fail(KVC_ERR_HIP, "sink_window_attention: launch failed");
+  return KVC_OK;
+}
+
+static int config_count(const kvc_cache* h) {
+  return h->kv_dtype == KVC_KV_FP8 ? 1 : kvc::attention_bf16_configs(h->D, nullptr, nullptr, 0);
+}
+
+int kv_cache_config_count(kvc_handle h, int* out_count) {
+  g_last_error.clear();
+  if (!h || !out_count) return fail(KVC_ERR_INVALID, "kv_cache_config_count: NULL handle or output");
+  *out_count = config_count(h);
+  return KVC_OK;
+}
+
+int kv_cache_config_info(kvc_handle h, int id, int* waves_per_workgroup, int* workgroups_per_cu) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "kv_cache_config_info: handle is NULL");
+  const int n = config_count(h);
+  if (id < 0 || id >= n) return fail(KVC_ERR_INVALID, "kv_cache_config_info: config %d outside [0, %d)", id, n);
+  int w = 8, g = 1;  // fp8: its one configuration
+  if (h->kv_dtype != KVC_KV_FP8) {
+    int ws[8], gs[8];
+    kvc::attention_bf16_configs(h->D, ws, gs, 8);
+    w = ws[id];
+    g = gs[id];
+  }
+  if (waves_per_workgroup) *waves_per_workgroup = w;
+  if (workgroups_per_cu) *workgroups_per_cu = g;
+  return KVC_OK;
+}
+
+int kv_cache_set_config(kvc_handle h, int id) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "kv_cache_set_config: handle is NULL");
+  const int n = config_count(h);
+  if (id < 0 || id >= n) return fail(KVC_ERR_INVALID, "kv_cache_set_config: config %d outside [0, %d)", id, n);
+  h->config = id;
+  return KVC_OK;
+}
+
+int kv_cache_get_config(kvc_handle h, int* out_id) {
+  g_last_error.clear();
+  if (!h || !out_id) return fail(KVC_ERR_INVALID, "kv_cache_get_config: NULL handle or output");
+  *out_id = h->config;
+  return KVC_OK;
+}
+
+int kv_cache_autotune(kvc_handle h, const void* q, const void* k_cur, const void* v_cur, void* o, int reps,
+                      void* stream, int* out_id, float* out_ms) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "kv_cache_autotune: handle is NULL");
+  if (reps < 1) return fail(KVC_ERR_INVALID, "kv_cache_autotune: reps = %d < 1", reps);
+  if (!q || !k_cur || !v_cur || !o) return fail(KVC_ERR_INVALID, "kv_cache_autotune: NULL q, k_cur, v_cur or o");
+  const int n = config_count(h);
+  const int before = h->config;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return fail(KVC_ERR_HIP, "kv_cache_autotune: hipEventCreate failed");
+  }
+  int best = before;
+  float best_ms = 0.f;
+  int rc = KVC_OK;
+  for (int id = 0; id < n && rc == KVC_OK; ++id) {
+    h->config = id;
+    rc = sink_window_attention(h, q, k_cur, v_cur, o, nullptr, 0.f, stream);  // warm-up
+    if (rc != KVC_OK) break;
+    if (hipEventRecord(e0, (hipStream_t)stream) != hipSuccess) rc = KVC_ERR_HIP;
+    for (int r = 0; r < reps && rc == KVC_OK; ++r) rc = sink_window_attention(h, q, k_cur, v_cur, o, nullptr, 0.f, stream);
+    if (rc != KVC_OK) break;
+    float ms = 0.f;
+    if (hipEventRecord(e1, (hipStream_t)stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+        hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+      rc = fail(KVC_ERR_HIP, "kv_cache_autotune: event timing failed");
+      break;
+    }
+    ms /= reps;
+    if (out_ms) out_ms[id] = ms;
+    if (id == 0 || ms < best_ms) {
+      best = id;
+      best_ms = ms;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (rc != KVC_OK) {
+    h->config = before;
+    return rc;
+  }
+  h->config = best;
+  if (out_id) *out_id = best;
   return KVC_OK;
 }
 
@@ -397,7 +489,7 @@ int sink_window_attention_chunks(kvc_handle h, int n_chunks, const void* q, cons
   if (kvc::launch_transpose_v_bf16((const uint16_t*)v, (uint16_t*)workspace, h->H, h->T, h->D, ws_rows, 0,
                                    (hipStream_t)stream, n_chunks, (int)T8) != 0)
     return fail(KVC_ERR_HIP, "sink_window_attention_chunks: transpose launch failed");
-  if (kvc::launch_attention_chunks_bf16(a, h->D, (hipStream_t)stream) != 0)
+  if (kvc::launch_attention_chunks_bf16(a, h->D, h->config, (hipStream_t)stream) != 0)
     return fail(KVC_ERR_HIP, "sink_window_attention_chunks: launch failed");
   return KVC_OK;
 }

@@ -67,15 +67,19 @@ struct AttnArgs {
   int32_t seg_blk[kMaxSegments];
 };
 
-// bf16 attention: one 8-wave workgroup per CU and (head, query tile of up to 256 rows).
+// bf16 attention: one workgroup per (head, query tile of up to 32 rows per wave).
 // Workspace of the split units: bytes of ws_o and ws_ml, and counters, for a
 // device with num_cus compute units.
 size_t attention_ws_o_bytes(int num_cus, int head_dim);
 size_t attention_ws_ml_bytes(int num_cus);
 int attention_ws_counters(int num_cus);
-int launch_attention_bf16(AttnArgs& a, int head_dim, hipStream_t stream);
+// config: index into the launch configurations of the head dim (0 = default);
+// attention_bf16_configs lists them (waves per workgroup, workgroups per CU)
+// and returns their number.
+int attention_bf16_configs(int head_dim, int* waves, int* wgs, int cap);
+int launch_attention_bf16(AttnArgs& a, int head_dim, int config, hipStream_t stream);
 // Whole-stream form: every (head, chunk, query tile) of n_chunks chunks in one launch.
-int launch_attention_chunks_bf16(AttnArgs& a, int head_dim, hipStream_t stream);
+int launch_attention_chunks_bf16(AttnArgs& a, int head_dim, int config, hipStream_t stream);
 
 // Copy K src [H][rows][D] (bf16) into rows [row0, row0 + rows) of a pool [H][pool_rows][D].
 int launch_rows_copy_bf16(const uint16_t* src, uint16_t* pool, int H, int rows, int D, int64_t pool_rows,

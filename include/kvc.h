@@ -211,6 +211,37 @@ int sink_window_attention_chunks(kvc_handle h, int n_chunks, const void* q, cons
 int kvc_chunks_workspace_bytes(kvc_handle h, int n_chunks, size_t* out_bytes);
 
 /*
+ * Launch configurations of the attention kernel (waves per workgroup x
+ * workgroups resident per CU).  bf16 caches: 8x1 and 4x2 at D = 128, 8x1,
+ * 4x2 and 4x3 at D = 64; fp8 caches: one.  Configuration 0 is the default.
+ * Which is fastest depends on H, T, the key count and D (how the units of
+ * work fill the CUs' slots, how many workgroups share one head's K/V stream),
+ * so it is measured rather than modelled.  Not described by the pages (they
+ * name auto-tuning among their deployment tools: zhichai.net post, deployment
+ * paragraph); these calls are this library's.
+ *
+ * kv_cache_config_count - number of configurations.  Errors: INVALID.
+ * kv_cache_config_info  - waves per workgroup and workgroups per CU of
+ *                         configuration id.  Errors: INVALID (bad id).
+ * kv_cache_set_config / kv_cache_get_config - the configuration later
+ *                         attention calls use.  Errors: INVALID (bad id).
+ * kv_cache_autotune - run sink_window_attention on these inputs (the cache's
+ *   current contents: call it at the state to tune for, e.g. a full window)
+ *   with every configuration: one warm-up and `reps` timed calls each (HIP
+ *   events on `stream`; the call waits for them), then keep the fastest.
+ *   o holds that last run's output (not necessarily the chosen
+ *   configuration's).  out_ms (NULL or count floats) receives the mean time
+ *   per call of each configuration.  The cache's slot table is unchanged.
+ *   Errors: INVALID, HIP (the previous configuration is kept).
+ */
+int kv_cache_config_count(kvc_handle h, int* out_count);
+int kv_cache_config_info(kvc_handle h, int id, int* waves_per_workgroup, int* workgroups_per_cu);
+int kv_cache_set_config(kvc_handle h, int id);
+int kv_cache_get_config(kvc_handle h, int* out_id);
+int kv_cache_autotune(kvc_handle h, const void* q, const void* k_cur, const void* v_cur, void* o, int reps,
+                      void* stream, int* out_id, float* out_ms);
+
+/*
  * kv_cache_pool_view - device addresses of the pool, for inspection (tests,
  * tools).  Read-only use; valid until destroy.  Any output may be NULL.
  *   rows     pool rows including the spare slot: round8(Lc) + (n_sink + W + 1) *

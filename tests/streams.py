@@ -51,15 +51,19 @@ def say(*a):
 
 def run_stream(spec: synthetic.StreamSpec, check: Iterable[int], rows: Optional[np.ndarray] = None,
                evict_plan: Optional[Dict[int, int]] = None,
-               max_abs: float = BF16_MAX_ABS, rel_l2: float = BF16_REL_L2, lse_tol: float = LSE_TOL):
+               max_abs: float = BF16_MAX_ABS, rel_l2: float = BF16_REL_L2, lse_tol: float = LSE_TOL,
+               config: Optional[int] = None):
     """Run chunks 0..max(check) of ``spec``; compare attention at the chunks in
-    ``check`` (every step, the given rows or all) and every append's indices."""
+    ``check`` (every step, the given rows or all) and every append's indices.
+    ``config`` selects the kernel's launch configuration."""
     import torch
     from block_causal_kv_amd import KVCache
 
     check = set(check)
     H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
     cache = KVCache(T, spec.window, spec.n_sink, spec.cond_len, H, D, spec.kv_dtype)
+    if config is not None:
+        cache.config = config
     model = CacheModel(spec.window, spec.n_sink)
     ck, cv = synthetic.cond_inputs(spec)
     cache.set_condition(to_dev(ck), to_dev(cv))

@@ -50,6 +50,13 @@ def test_create_rejects_bad_arguments_without_touching_the_gpu():
                                             None) == _lib.KVC_ERR_INVALID
     assert lib.sink_window_attention_rows(None, 5, None, None, None, None, None, 0.0, None) == _lib.KVC_ERR_INVALID
     assert lib.kv_cache_set_condition_rows(None, 0, None, None, None) == _lib.KVC_ERR_INVALID
+    i = C.c_int(-3)
+    assert lib.kv_cache_config_count(None, C.byref(i)) == _lib.KVC_ERR_INVALID
+    assert lib.kv_cache_config_info(None, 0, None, None) == _lib.KVC_ERR_INVALID
+    assert lib.kv_cache_set_config(None, 0) == _lib.KVC_ERR_INVALID
+    assert lib.kv_cache_get_config(None, C.byref(i)) == _lib.KVC_ERR_INVALID
+    assert lib.kv_cache_autotune(None, None, None, None, None, 1, None, None, None) == _lib.KVC_ERR_INVALID
+    assert i.value == -3
     n = C.c_size_t(7)
     assert lib.kvc_chunks_workspace_bytes(None, 2, C.byref(n)) == _lib.KVC_ERR_INVALID
     assert n.value == 7

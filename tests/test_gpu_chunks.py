@@ -27,9 +27,11 @@ def _inputs(spec, n):
     return qs, ks, vs
 
 
-def _cache(spec):
+def _cache(spec, config=None):
     from block_causal_kv_amd import KVCache
     cache = KVCache(spec.chunk_tokens, spec.window, spec.n_sink, spec.cond_len, spec.heads, spec.head_dim)
+    if config is not None:
+        cache.config = config
     ck, cv = synthetic.cond_inputs(spec)
     cache.set_condition(to_dev(ck), to_dev(cv))
     return cache, ck, cv
@@ -44,12 +46,12 @@ def _check(og, lg, ref, ref_lse, what):
     assert le <= LSE_TOL, (what, le)
 
 
-def run_chunks(spec, n, full_mask=True, chunks=None, rows=None, heads=None):
+def run_chunks(spec, n, full_mask=True, chunks=None, rows=None, heads=None, config=None):
     """Attention of chunks 0..n-1 of ``spec`` in one call; compare every chunk
     (``full_mask``) or the given chunks / rows / heads (per-chunk oracle)."""
     import torch
     H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
-    cache, ck, cv = _cache(spec)
+    cache, ck, cv = _cache(spec, config)
     qs, ks, vs = _inputs(spec, n)
     cat = lambda xs: np.concatenate(xs, axis=1)
     say("  %s: %d chunks in one call, H=%d T=%d D=%d Lc=%d W=%d sink=%d"
