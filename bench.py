@@ -265,6 +265,8 @@ def main() -> int:
     ap.add_argument("--flatness", action="store_true",
                     help="stream the 300-chunk long config from an empty cache and report per-chunk "
                          "latency flatness and device memory instead of the throughput line")
+    ap.add_argument("--no-autotune", action="store_true",
+                    help="keep the default launch configuration instead of timing each once before the run")
     ap.add_argument("--chunks", type=int, default=0,
                     help="time the whole-stream form instead: every chunk of an N-chunk stream in one call")
     args = ap.parse_args()
@@ -321,6 +323,15 @@ def main() -> int:
     for i in range(spec.n_sink + spec.window):
         s = sets[i % len(sets)]
         cache.append_chunk(s["kc"], s["vc"], stream=stream)
+    # launch configuration: measured on a steady-state call before the run
+    tuned = None
+    if not args.no_autotune and spec.kv_dtype == "bf16":
+        s0 = sets[0]
+        best, tms = cache.autotune(s0["q"][0], s0["k"][0], s0["v"][0], out=out, reps=5, stream=stream)
+        tuned = {"chosen": best, "ms_per_config": [round(t, 4) for t in tms]}
+    cfgs = cache.configs()
+    kernel_cfg = {"id": cache.config, "waves_per_workgroup": cfgs[cache.config][0],
+                  "workgroups_per_cu": cfgs[cache.config][1], "autotune": tuned}
     for i in range(args.warmup):
         chunk_step(i)
     torch.cuda.synchronize()
@@ -364,7 +375,7 @@ def main() -> int:
         "config": {"workload": workload_name(spec), "chunk_tokens": T, "cond_len": spec.cond_len,
                    "heads": H, "head_dim": D, "window": spec.window, "n_sink": spec.n_sink,
                    "kv_len": spec.steady_kv_len(), "calls_per_step": spec.steps,
-                   "input_sets": args.sets},
+                   "input_sets": args.sets, "kernel_config": kernel_cfg},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "attention_ms_per_call": round(attn_avg, 4),
         "attention_ms_p50_p99_max": [round(float(np.percentile(attn_ms, p)), 4) for p in (50, 99, 100)],
