@@ -25,22 +25,39 @@ def _stream_ptr(stream) -> Optional[int]:
 
 
 class KVCache:
-    """Owner of one bounded KV cache (``kv_cache_create`` ... ``kv_cache_destroy``)."""
+    """Owner of one bounded KV cache (``kv_cache_create_layers`` ... ``kv_cache_destroy``).
+
+    With ``layers`` > 1 the cache serves the attention layers of a model: one
+    slot table, condition writes and appends for all layers at once (tensors
+    [layers * H][n][D]), and per-layer attention through ``layer(l)``."""
 
     def __init__(self, chunk_tokens: int, window: int, n_sink: int = 1, cond_len: int = 0,
-                 heads: int = 1, head_dim: int = 128, kv_dtype: str = "bf16"):
+                 heads: int = 1, head_dim: int = 128, kv_dtype: str = "bf16", layers: int = 1):
         self._lib = load()
         self.T, self.W, self.n_sink, self.Lc = chunk_tokens, window, n_sink, cond_len
-        self.H, self.D, self.kv_dtype = heads, head_dim, kv_dtype
+        self.H, self.D, self.kv_dtype, self.layers = heads, head_dim, kv_dtype, layers
+        self._wh = heads * layers  # heads of a condition or chunk write through this handle
+        self._views = {}
         h = C.c_void_p()
-        check(self._lib.kv_cache_create(chunk_tokens, window, n_sink, cond_len, heads, head_dim,
-                                        _DTYPES[kv_dtype], C.byref(h)))
+        check(self._lib.kv_cache_create_layers(chunk_tokens, window, n_sink, cond_len, heads, head_dim,
+                                               _DTYPES[kv_dtype], layers, C.byref(h)))
         self._h = h
+
+    def layer(self, index: int) -> "KVCache":
+        """The view of one layer (``kv_cache_layer``): attention, its condition,
+        ``write_chunk``; freed with this cache."""
+        if index not in self._views:
+            v = C.c_void_p()
+            check(self._lib.kv_cache_layer(self._h, index, C.byref(v)))
+            self._views[index] = _LayerView(self, v)
+        return self._views[index]
 
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value is not None:
             check(self._lib.kv_cache_destroy(self._h))
             self._h = None
+            for v in self._views.values():
+                v._h = None
 
     def __del__(self):
         try:
@@ -55,15 +72,16 @@ class KVCache:
         self.close()
 
     # ---- tensor checks (marshalling)
-    def _check(self, t, rows: int, name: str, dtype=None):
+    def _check(self, t, rows: int, name: str, dtype=None, heads: Optional[int] = None):
         import torch
         dtype = torch.bfloat16 if dtype is None else dtype
+        heads = self.H if heads is None else heads
         if t is None:
             raise ValueError("%s is None" % name)
         if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
             raise ValueError("%s must be a contiguous %s CUDA tensor" % (name, dtype))
-        if tuple(t.shape) != (self.H, rows, self.D):
-            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (self.H, rows, self.D)))
+        if tuple(t.shape) != (heads, rows, self.D):
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (heads, rows, self.D)))
         return C.c_void_p(t.data_ptr())
 
     def set_condition(self, k, v, stream=None) -> None:
@@ -72,16 +90,30 @@ class KVCache:
         n = k.shape[1] if k is not None and k.dim() == 3 else self.Lc
         if n > self.Lc:
             raise ValueError("condition of %d rows exceeds Lc = %d" % (n, self.Lc))
-        kp = self._check(k, n, "k_cond") if n > 0 else None
-        vp = self._check(v, n, "v_cond") if n > 0 else None
+        kp = self._check(k, n, "k_cond", heads=self._wh) if n > 0 else None
+        vp = self._check(v, n, "v_cond", heads=self._wh) if n > 0 else None
         check(self._lib.kv_cache_set_condition_rows(self._h, n, kp, vp, C.c_void_p(_stream_ptr(stream))))
 
     def append_chunk(self, k, v, stream=None) -> Tuple[int, int, int]:
+        """Write the clean K/V of the chunk just generated (all layers) and record
+        it; returns (chunk id, slot, evicted chunk or -1)."""
         cid, slot, ev = C.c_int64(), C.c_int(), C.c_int64()
-        check(self._lib.kv_cache_append_chunk(self._h, self._check(k, self.T, "k"),
-                                              self._check(v, self.T, "v"),
+        check(self._lib.kv_cache_append_chunk(self._h, self._check(k, self.T, "k", heads=self._wh),
+                                              self._check(v, self.T, "v", heads=self._wh),
                                               C.c_void_p(_stream_ptr(stream)), C.byref(cid),
                                               C.byref(slot), C.byref(ev)))
+        return cid.value, slot.value, ev.value
+
+    def write_chunk(self, k, v, stream=None) -> None:
+        """Write this handle's part of the chunk about to be appended, without
+        recording it (``kv_cache_write_chunk``); then ``append_commit``."""
+        check(self._lib.kv_cache_write_chunk(self._h, self._check(k, self.T, "k", heads=self._wh),
+                                             self._check(v, self.T, "v", heads=self._wh),
+                                             C.c_void_p(_stream_ptr(stream))))
+
+    def append_commit(self) -> Tuple[int, int, int]:
+        cid, slot, ev = C.c_int64(), C.c_int(), C.c_int64()
+        check(self._lib.kv_cache_append_commit(self._h, C.byref(cid), C.byref(slot), C.byref(ev)))
         return cid.value, slot.value, ev.value
 
     def evict(self, n: int) -> List[int]:
@@ -203,6 +235,24 @@ class KVCache:
                                                      C.c_void_p(workspace.data_ptr()), C.c_size_t(wbytes),
                                                      C.c_void_p(_stream_ptr(stream))))
         return out
+
+
+class _LayerView(KVCache):
+    """One layer of a multi-layer cache (``kv_cache_layer``); owned by the cache."""
+
+    def __init__(self, cache: KVCache, handle):  # noqa: super().__init__ creates a cache
+        self._lib = cache._lib
+        self.T, self.W, self.n_sink, self.Lc = cache.T, cache.W, cache.n_sink, cache.Lc
+        self.H, self.D, self.kv_dtype, self.layers = cache.H, cache.D, cache.kv_dtype, 1
+        self._wh = cache.H
+        self._views = {}
+        self._h = handle
+
+    def layer(self, index: int) -> "KVCache":
+        raise KVCError(_lib.KVC_ERR_INVALID, "a layer view has no layers")
+
+    def close(self) -> None:  # freed with the cache
+        self._h = None
 
 
 class SlotTable:

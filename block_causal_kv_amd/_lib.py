@@ -23,6 +23,12 @@ SIGNATURES = {
     "kv_cache_query": (C.c_int, [C.c_void_p, _I64P, _IP, _I64P, C.c_int]),
     "sink_window_attention": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                         C.c_void_p, C.c_float, C.c_void_p]),
+    "kv_cache_create_layers": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int,
+                                         C.POINTER(C.c_void_p)]),
+    "kv_cache_layer": (C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_void_p)]),
+    "kv_cache_write_chunk": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
+    "kv_cache_append_commit": (C.c_int, [C.c_void_p, C.POINTER(C.c_int64), C.POINTER(C.c_int),
+                                         C.POINTER(C.c_int64)]),
     "sink_window_attention_rows": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
                                              C.c_void_p, C.c_void_p, C.c_float, C.c_void_p]),
     "kv_cache_set_condition_rows": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]),

@@ -11,6 +11,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "../../include/kvc.h"
 #include "launch.h"
@@ -38,27 +39,41 @@ int hip_fail(hipError_t e, const char* what) {
 
 struct kvc_cache {
   int T, W, n_sink, Lc, H, D, kv_dtype;
-  int cond_rows;  // condition rows in use (<= Lc): the last kv_cache_set_condition_rows
   int device;
   // Pool rows: condition rows [0, Lc), slot s at SlotTable::slot_row0(s, T, Lc)
   // (starts rounded up to multiples of 8), then one spare slot at cur_row0 for
-  // the current chunk (V^T in bf16 caches, K and V codes in fp8 caches).
+  // the current chunk (V^T in bf16 caches, K and V codes in fp8 caches).  A
+  // cache of L layers holds L * H heads, layer l's heads at l * H.
   int64_t pool_rows;      // cur_row0: rows of the condition and the n_sink + W slots
   int64_t spare_rows;     // pool_rows + round8(T)
-  void* k_pool = nullptr;  // bf16: K [H][pool_rows][D].  fp8: K codes [H][spare_rows][D]
-  void* v_pool = nullptr;  // bf16: V^T [H][D][spare_rows].  fp8: V^T codes [H][D][spare_rows]
+  void* k_pool = nullptr;  // bf16: K [heads][pool_rows][D].  fp8: K codes [heads][spare_rows][D]
+  void* v_pool = nullptr;  // bf16: V^T [heads][D][spare_rows].  fp8: V^T codes [heads][D][spare_rows]
   size_t k_bytes = 0, v_bytes = 0;
-  float* scales = nullptr;    // fp8: [2][H][blocks]: block 0 = condition, 1 + s = slot s, last = current
-  uint32_t* amax = nullptr;   // fp8: [2][H] scratch of the quantiser
+  float* scales = nullptr;    // fp8: [2][L*H][blocks]: block 0 = condition, 1 + s = slot s, last = current
+  int scale_tensor = 0;       // fp8: L * H * blocks (offset of the V scales)
+  uint32_t* amax = nullptr;   // fp8: [2][L*H] scratch of the quantiser
   int blocks() const { return n_sink + W + 2; }
   int num_cus = 0;
   float* ws_o = nullptr;   // attention workspace: partials of split query tiles
   float* ws_ml = nullptr;
   int* ws_cnt = nullptr;
   int config = 0;  // bf16 attention launch configuration (kv_cache_set_config)
-  kvc::SlotTable table;
+  // Layers.  The root handle owns the pools, the slot table and the layer
+  // views; a view (kv_cache_layer) points at its layer's heads in the pools.
+  int layers = 1;
+  int layer = 0;
+  kvc_cache* root = nullptr;          // a view's cache; nullptr for the root
+  std::vector<kvc_cache*> views;      // root: views made so far (freed with it)
+  std::vector<int> cond_rows_l;       // root: condition rows in use per layer
+  kvc::SlotTable table;               // root's slot table (views use the root's)
+  kvc::SlotTable& tbl() { return root ? root->table : table; }
+  kvc_cache* top() { return root ? root : this; }
+  // heads written by a condition write or a chunk write through this handle
+  int heads_written() const { return root ? H : H * layers; }
+  // condition rows in use for attention through this handle (a root of one layer, or a view)
+  int cond_rows() { return top()->cond_rows_l[root ? layer : 0]; }
   kvc_cache(int T_, int W_, int S_, int Lc_, int H_, int D_, int dt)
-      : T(T_), W(W_), n_sink(S_), Lc(Lc_), H(H_), D(D_), kv_dtype(dt), cond_rows(Lc_), device(0),
+      : T(T_), W(W_), n_sink(S_), Lc(Lc_), H(H_), D(D_), kv_dtype(dt), device(0),
         pool_rows(kvc::SlotTable::slot_row0(S_ + W_, T_, Lc_)),
         spare_rows(pool_rows + kvc::SlotTable::round8(T_)), table(W_, S_) {}
 };
@@ -72,18 +87,33 @@ namespace {
 
 // fp8 cache: quantise K/V bf16 [H][rows][D] into pool rows [row0, row0 + rows) with scale block blk.
 int quantize_into(kvc_cache* h, const void* k, const void* v, int rows, int row0, int blk, hipStream_t st) {
-  return kvc::launch_quantize_fp8((const uint16_t*)k, (const uint16_t*)v, h->H, rows, h->D, h->amax,
-                                  (uint8_t*)h->k_pool, h->spare_rows * h->D, (uint8_t*)h->v_pool, h->spare_rows, row0,
-                                  h->scales + blk, h->H * h->blocks(), h->blocks(), st);
+  return kvc::launch_quantize_fp8((const uint16_t*)k, (const uint16_t*)v, h->heads_written(), rows, h->D,
+                                  h->amax, (uint8_t*)h->k_pool, h->spare_rows * h->D, (uint8_t*)h->v_pool,
+                                  h->spare_rows, row0, h->scales + blk, h->scale_tensor, h->blocks(), st);
 }
 
 // bf16 cache: K rows copied to pool rows [row0, row0 + rows), V written transposed to columns row0...
 int write_bf16(kvc_cache* h, const void* k, const void* v, int rows, int row0, hipStream_t st) {
-  if (kvc::launch_rows_copy_bf16((const uint16_t*)k, (uint16_t*)h->k_pool, h->H, rows, h->D, h->pool_rows, row0,
+  const int heads = h->heads_written();
+  if (kvc::launch_rows_copy_bf16((const uint16_t*)k, (uint16_t*)h->k_pool, heads, rows, h->D, h->pool_rows, row0,
                                  st) != 0)
     return -1;
-  return kvc::launch_transpose_v_bf16((const uint16_t*)v, (uint16_t*)h->v_pool, h->H, rows, h->D,
+  return kvc::launch_transpose_v_bf16((const uint16_t*)v, (uint16_t*)h->v_pool, heads, rows, h->D,
                                       h->spare_rows, row0, st);
+}
+
+// The chunk about to be appended, written for this handle's heads into the
+// slot the next append takes (not committed).
+int write_chunk(kvc_cache* h, const void* k, const void* v, hipStream_t st, int* out_slot, int64_t* out_evicted) {
+  int slot;
+  int64_t evicted;
+  h->tbl().plan_append(&slot, &evicted);
+  const int row0 = kvc::SlotTable::slot_row0(slot, h->T, h->Lc);
+  const int rc = h->kv_dtype == KVC_KV_FP8 ? quantize_into(h, k, v, h->T, row0, 1 + slot, st)
+                                           : write_bf16(h, k, v, h->T, row0, st);
+  if (out_slot) *out_slot = slot;
+  if (out_evicted) *out_evicted = evicted;
+  return rc;
 }
 
 }  // namespace
@@ -94,8 +124,16 @@ const char* kvc_last_error(void) { return g_last_error.c_str(); }
 
 int kv_cache_create(int chunk_tokens, int window_w, int n_sink, int cond_len, int heads,
                     int head_dim, int kv_dtype, kvc_handle* out) {
+  return kv_cache_create_layers(chunk_tokens, window_w, n_sink, cond_len, heads, head_dim, kv_dtype, 1, out);
+}
+
+int kv_cache_create_layers(int chunk_tokens, int window_w, int n_sink, int cond_len, int heads,
+                           int head_dim, int kv_dtype, int layers, kvc_handle* out) {
   g_last_error.clear();
   if (!out) return fail(KVC_ERR_INVALID, "kv_cache_create: out is NULL");
+  if (layers < 1) return fail(KVC_ERR_INVALID, "kv_cache_create: layers = %d < 1", layers);
+  if ((int64_t)heads * layers > (1 << 20))
+    return fail(KVC_ERR_INVALID, "kv_cache_create: %d layers x %d heads is too many", layers, heads);
   if (chunk_tokens < 1 || window_w < 1 || n_sink < 0 || cond_len < 0 || heads < 1)
     return fail(KVC_ERR_INVALID,
                 "kv_cache_create: need T >= 1, W >= 1, n_sink >= 0, Lc >= 0, H >= 1 "
@@ -116,12 +154,16 @@ int kv_cache_create(int chunk_tokens, int window_w, int n_sink, int cond_len, in
   // stay below 2^31 bytes (32-bit buffer offsets) and so must T * H rows
   const int64_t T8 = ((int64_t)chunk_tokens + 7) & ~7LL, Lc8 = ((int64_t)cond_len + 7) & ~7LL;
   const int64_t spare_rows = Lc8 + (int64_t)(n_sink + window_w + 1) * T8;
-  if (spare_rows * head_dim * 2 > INT32_MAX || (int64_t)chunk_tokens * heads * head_dim * 2 > INT32_MAX)
+  if (spare_rows * head_dim * 2 > INT32_MAX ||
+      (int64_t)chunk_tokens * heads * layers * head_dim * 2 > INT32_MAX)
     return fail(KVC_ERR_INVALID, "kv_cache_create: sizes overflow 32-bit offsets (T=%d Lc=%d slots=%d D=%d)",
                 chunk_tokens, cond_len, n_sink + window_w, head_dim);
   kvc_cache* c = new (std::nothrow) kvc_cache(chunk_tokens, window_w, n_sink, cond_len, heads,
                                               head_dim, kv_dtype);
   if (!c) return fail(KVC_ERR_OOM, "kv_cache_create: host allocation failed");
+  c->layers = layers;
+  c->cond_rows_l.assign(layers, cond_len);
+  const int all_heads = heads * layers;
   hipError_t e = hipGetDevice(&c->device);
   if (e != hipSuccess) {
     delete c;
@@ -133,21 +175,16 @@ int kv_cache_create(int chunk_tokens, int window_w, int n_sink, int cond_len, in
     return hip_fail(e, "kv_cache_create: hipDeviceGetAttribute");
   }
   const bool fp8 = kv_dtype == KVC_KV_FP8;
-  const size_t hd = (size_t)heads * (size_t)head_dim;
-  // fp8 code pools carry 64 spare bytes past the last row (the fp8 kernel's loads are range-checked
-  // against the allocation, not per head)
+  const size_t hd = (size_t)all_heads * (size_t)head_dim;
+  // fp8 code pools carry 64 spare bytes past the last row
   c->k_bytes = fp8 ? hd * (size_t)c->spare_rows + 64 : hd * (size_t)c->pool_rows * 2;
   c->v_bytes = fp8 ? hd * (size_t)c->spare_rows + 64 : hd * (size_t)c->spare_rows * 2;
-  if (fp8 && c->k_bytes > (size_t)INT32_MAX) {
-    const size_t kb = c->k_bytes;
-    delete c;
-    return fail(KVC_ERR_INVALID, "kv_cache_create: fp8 code pool of %zu bytes exceeds 2^31", kb);
-  }
+  c->scale_tensor = all_heads * c->blocks();
   e = hipMalloc(&c->k_pool, c->k_bytes);
   if (e == hipSuccess) e = hipMalloc(&c->v_pool, c->v_bytes);
-  if (e == hipSuccess && fp8) e = hipMalloc(&c->scales, sizeof(float) * 2 * heads * c->blocks());
-  if (e == hipSuccess && fp8) e = hipMalloc(&c->amax, sizeof(uint32_t) * 2 * heads);
-  if (e == hipSuccess && fp8) e = hipMemset(c->scales, 0, sizeof(float) * 2 * heads * c->blocks());
+  if (e == hipSuccess && fp8) e = hipMalloc(&c->scales, sizeof(float) * 2 * all_heads * c->blocks());
+  if (e == hipSuccess && fp8) e = hipMalloc(&c->amax, sizeof(uint32_t) * 2 * all_heads);
+  if (e == hipSuccess && fp8) e = hipMemset(c->scales, 0, sizeof(float) * 2 * all_heads * c->blocks());
   const int n_cnt = kvc::attention_ws_counters(c->num_cus);
   if (e == hipSuccess) e = hipMalloc(&c->ws_o, kvc::attention_ws_o_bytes(c->num_cus, head_dim));
   if (e == hipSuccess) e = hipMalloc(&c->ws_ml, kvc::attention_ws_ml_bytes(c->num_cus));
@@ -175,6 +212,8 @@ int kv_cache_create(int chunk_tokens, int window_w, int n_sink, int cond_len, in
 int kv_cache_destroy(kvc_handle h) {
   g_last_error.clear();
   if (!h) return KVC_OK;
+  if (h->root) return fail(KVC_ERR_INVALID, "kv_cache_destroy: a layer view is freed with its cache");
+  for (kvc_cache* v : h->views) delete v;
   int rc = KVC_OK;
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) rc = hip_fail(e, "kv_cache_destroy: hipDeviceSynchronize");
@@ -183,6 +222,69 @@ int kv_cache_destroy(kvc_handle h) {
     if (p) (void)hipFree(p);
   delete h;
   return rc;
+}
+
+int kv_cache_layer(kvc_handle h, int layer, kvc_handle* out_view) {
+  g_last_error.clear();
+  if (!h || !out_view) return fail(KVC_ERR_INVALID, "kv_cache_layer: NULL handle or output");
+  if (h->root) return fail(KVC_ERR_INVALID, "kv_cache_layer: the handle is already a layer view");
+  if (layer < 0 || layer >= h->layers)
+    return fail(KVC_ERR_INVALID, "kv_cache_layer: layer %d outside [0, %d)", layer, h->layers);
+  for (kvc_cache* v : h->views)
+    if (v->layer == layer) {
+      *out_view = v;
+      return KVC_OK;
+    }
+  kvc_cache* v = new (std::nothrow) kvc_cache(h->T, h->W, h->n_sink, h->Lc, h->H, h->D, h->kv_dtype);
+  if (!v) return fail(KVC_ERR_OOM, "kv_cache_layer: host allocation failed");
+  const bool fp8 = h->kv_dtype == KVC_KV_FP8;
+  const size_t heads0 = (size_t)layer * h->H;  // first head of the layer
+  v->root = h;
+  v->layer = layer;
+  v->layers = 1;
+  v->device = h->device;
+  v->num_cus = h->num_cus;
+  v->config = h->config;
+  v->k_pool = (uint8_t*)h->k_pool + heads0 * h->D * (fp8 ? (size_t)h->spare_rows : (size_t)h->pool_rows * 2);
+  v->v_pool = (uint8_t*)h->v_pool + heads0 * h->D * (size_t)h->spare_rows * (fp8 ? 1 : 2);
+  v->scales = fp8 ? h->scales + heads0 * h->blocks() : nullptr;
+  v->scale_tensor = h->scale_tensor;
+  v->amax = h->amax;
+  v->ws_o = h->ws_o;
+  v->ws_ml = h->ws_ml;
+  v->ws_cnt = h->ws_cnt;
+  try {
+    h->views.push_back(v);
+  } catch (...) {
+    delete v;
+    return fail(KVC_ERR_OOM, "kv_cache_layer: host allocation failed");
+  }
+  *out_view = v;
+  return KVC_OK;
+}
+
+int kv_cache_write_chunk(kvc_handle h, const void* k, const void* v, void* stream) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "kv_cache_write_chunk: handle is NULL");
+  if (!k || !v) return fail(KVC_ERR_INVALID, "kv_cache_write_chunk: NULL K or V");
+  if (write_chunk(h, k, v, (hipStream_t)stream, nullptr, nullptr) != 0)
+    return fail(KVC_ERR_HIP, "kv_cache_write_chunk: launch failed");
+  return KVC_OK;
+}
+
+int kv_cache_append_commit(kvc_handle h, int64_t* out_chunk_id, int* out_slot, int64_t* out_evicted) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "kv_cache_append_commit: handle is NULL");
+  if (h->root) return fail(KVC_ERR_STATE, "kv_cache_append_commit: commit through the cache, not a layer view");
+  int slot;
+  int64_t evicted;
+  h->table.plan_append(&slot, &evicted);
+  const int64_t id = h->table.next_chunk_id();
+  h->table.commit_append(slot);
+  if (out_chunk_id) *out_chunk_id = id;
+  if (out_slot) *out_slot = slot;
+  if (out_evicted) *out_evicted = evicted;
+  return KVC_OK;
 }
 
 int kv_cache_set_condition_rows(kvc_handle h, int n, const void* k_cond, const void* v_cond, void* stream) {
@@ -198,7 +300,11 @@ int kv_cache_set_condition_rows(kvc_handle h, int n, const void* k_cond, const v
                                              : write_bf16(h, k_cond, v_cond, n, 0, (hipStream_t)stream);
     if (rc != 0) return fail(KVC_ERR_HIP, "kv_cache_set_condition_rows: launch failed");
   }
-  h->cond_rows = n;
+  kvc_cache* r = h->top();
+  if (h->root)
+    r->cond_rows_l[h->layer] = n;
+  else
+    for (int& c : r->cond_rows_l) c = n;
   return KVC_OK;
 }
 
@@ -212,25 +318,20 @@ int kv_cache_append_chunk(kvc_handle h, const void* k, const void* v, void* stre
                           int64_t* out_chunk_id, int* out_slot, int64_t* out_evicted) {
   g_last_error.clear();
   if (!h) return fail(KVC_ERR_INVALID, "kv_cache_append_chunk: handle is NULL");
+  if (h->root)
+    return fail(KVC_ERR_STATE,
+                "kv_cache_append_chunk: append through the cache (all layers), or kv_cache_write_chunk per "
+                "layer then kv_cache_append_commit");
   if (!k || !v) return fail(KVC_ERR_INVALID, "kv_cache_append_chunk: NULL K or V");
-  int slot;
-  int64_t evicted;
-  h->table.plan_append(&slot, &evicted);
-  const int row0 = kvc::SlotTable::slot_row0(slot, h->T, h->Lc);
-  const int rc = h->kv_dtype == KVC_KV_FP8 ? quantize_into(h, k, v, h->T, row0, 1 + slot, (hipStream_t)stream)
-                                           : write_bf16(h, k, v, h->T, row0, (hipStream_t)stream);
-  if (rc != 0) return fail(KVC_ERR_HIP, "kv_cache_append_chunk: launch failed");
-  const int64_t id = h->table.next_chunk_id();
-  h->table.commit_append(slot);
-  if (out_chunk_id) *out_chunk_id = id;
-  if (out_slot) *out_slot = slot;
-  if (out_evicted) *out_evicted = evicted;
-  return KVC_OK;
+  if (write_chunk(h, k, v, (hipStream_t)stream, nullptr, nullptr) != 0)
+    return fail(KVC_ERR_HIP, "kv_cache_append_chunk: launch failed");
+  return kv_cache_append_commit(h, out_chunk_id, out_slot, out_evicted);
 }
 
 int kv_cache_evict(kvc_handle h, int n, int64_t* out_ids, int* out_n) {
   g_last_error.clear();
   if (!h) return fail(KVC_ERR_INVALID, "kv_cache_evict: handle is NULL");
+  if (h->root) return fail(KVC_ERR_STATE, "kv_cache_evict: evict through the cache, not a layer view");
   if (n < 0) return fail(KVC_ERR_INVALID, "kv_cache_evict: n = %d < 0", n);
   if (n > h->table.window_count())
     return fail(KVC_ERR_STATE, "kv_cache_evict: %d requested, %d window chunks held", n,
@@ -243,6 +344,7 @@ int kv_cache_evict(kvc_handle h, int n, int64_t* out_ids, int* out_n) {
 int kv_cache_reset(kvc_handle h) {
   g_last_error.clear();
   if (!h) return fail(KVC_ERR_INVALID, "kv_cache_reset: handle is NULL");
+  if (h->root) return fail(KVC_ERR_STATE, "kv_cache_reset: reset through the cache, not a layer view");
   h->table.reset();
   return KVC_OK;
 }
@@ -251,10 +353,11 @@ int kv_cache_query(kvc_handle h, int64_t* next_chunk_id, int* occupancy, int64_t
                    int cap) {
   g_last_error.clear();
   if (!h) return fail(KVC_ERR_INVALID, "kv_cache_query: handle is NULL");
-  if (next_chunk_id) *next_chunk_id = h->table.next_chunk_id();
-  if (occupancy) *occupancy = h->table.occupancy();
+  kvc::SlotTable& t = h->tbl();
+  if (next_chunk_id) *next_chunk_id = t.next_chunk_id();
+  if (occupancy) *occupancy = t.occupancy();
   if (slot_chunk)
-    for (int s = 0; s < h->table.n_slots() && s < cap; ++s) slot_chunk[s] = h->table.slot_chunk(s);
+    for (int s = 0; s < t.n_slots() && s < cap; ++s) slot_chunk[s] = t.slot_chunk(s);
   return KVC_OK;
 }
 
@@ -273,6 +376,9 @@ int sink_window_attention_rows(kvc_handle h, int n_q, const void* q, const void*
     return fail(KVC_ERR_INVALID, "sink_window_attention: NULL q, k_cur, v_cur or o");
   if (n_q < 1 || (int64_t)n_q * h->D * 2 > INT32_MAX || (int64_t)h->H * ((n_q + 255) / 256) > INT32_MAX)
     return fail(KVC_ERR_INVALID, "sink_window_attention: %d query rows (need 1 .. 32-bit offsets)", n_q);
+  if (!h->root && h->layers > 1)
+    return fail(KVC_ERR_STATE, "sink_window_attention: a cache of %d layers attends through a layer view "
+                "(kv_cache_layer)", h->layers);
   if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)h->D);
   if (!std::isfinite(scale)) return fail(KVC_ERR_INVALID, "sink_window_attention: scale not finite");
   kvc::AttnArgs a;
@@ -298,7 +404,7 @@ int sink_window_attention_rows(kvc_handle h, int n_q, const void* q, const void*
   if (h->kv_dtype == KVC_KV_FP8) {
     // every chunk has its own scales: one segment per block, the current chunk
     // quantised into the spare slot after the window slots
-    const std::vector<kvc::Segment> segs = h->table.segments(h->T, h->Lc, false, h->cond_rows);
+    const std::vector<kvc::Segment> segs = h->tbl().segments(h->T, h->Lc, false, h->cond_rows());
     if ((int)segs.size() + 1 > kvc::kMaxSegments)
       return fail(KVC_ERR_STATE, "sink_window_attention: %zu segments", segs.size());
     const int n_slots = h->n_sink + h->W;
@@ -318,7 +424,7 @@ int sink_window_attention_rows(kvc_handle h, int n_q, const void* q, const void*
     a.vt8 = (const uint8_t*)h->v_pool;
     a.pool_rows8 = h->spare_rows;
     a.scales = h->scales;
-    a.scale_tensor = h->H * h->blocks();
+    a.scale_tensor = h->scale_tensor;
     a.scale_head = h->blocks();
     if (quantize_into(h, k_cur, v_cur, h->T, cur_row0, n_slots + 1, (hipStream_t)stream) != 0)
       return fail(KVC_ERR_HIP, "sink_window_attention: quantise launch failed");
@@ -326,7 +432,7 @@ int sink_window_attention_rows(kvc_handle h, int n_q, const void* q, const void*
       return fail(KVC_ERR_HIP, "sink_window_attention: launch failed");
     return KVC_OK;
   }
-  const std::vector<kvc::Segment> segs = h->table.segments(h->T, h->Lc, true, h->cond_rows);
+  const std::vector<kvc::Segment> segs = h->tbl().segments(h->T, h->Lc, true, h->cond_rows());
   if ((int)segs.size() > kvc::kMaxSegments)
     return fail(KVC_ERR_STATE, "sink_window_attention: %zu segments", segs.size());
   a.nseg = (int)segs.size();
@@ -450,6 +556,9 @@ int sink_window_attention_chunks(kvc_handle h, int n_chunks, const void* q, cons
   if (h->kv_dtype != KVC_KV_BF16)
     return fail(KVC_ERR_UNSUPPORTED, "sink_window_attention_chunks: bf16 caches only");
   if (n_chunks < 1) return fail(KVC_ERR_INVALID, "sink_window_attention_chunks: n_chunks = %d < 1", n_chunks);
+  if (!h->root && h->layers > 1)
+    return fail(KVC_ERR_STATE, "sink_window_attention_chunks: a cache of %d layers attends through a layer view",
+                h->layers);
   if (!q || !k || !v || !o || !workspace)
     return fail(KVC_ERR_INVALID, "sink_window_attention_chunks: NULL q, k, v, o or workspace");
   const int64_t T8 = kvc::SlotTable::round8(h->T);
@@ -480,7 +589,7 @@ int sink_window_attention_chunks(kvc_handle h, int n_chunks, const void* q, cons
   a.n_chunks = n_chunks;
   a.window = h->W;
   a.n_sink = h->n_sink;
-  a.cond_len = h->cond_rows;
+  a.cond_len = h->cond_rows();
   a.t8 = (int)T8;
   a.kin = (const uint16_t*)k;
   a.vt_ws = (const uint16_t*)workspace;

@@ -80,6 +80,49 @@ const char* kvc_last_error(void);
 int kv_cache_create(int chunk_tokens, int window_w, int n_sink, int cond_len, int heads,
                     int head_dim, int kv_dtype, kvc_handle* out);
 
+/*
+ * kv_cache_create_layers - one cache for the L attention layers of a model:
+ * one slot table (every layer appends and evicts the same chunks), one pool
+ * of L x H heads, layer l's heads at l x H.  kv_cache_create is this call
+ * with layers = 1.  Source: the pages' model is a multi-layer MM-DiT whose
+ * every attention layer keeps the bounded cache (tutorial, "Hardware-software
+ * co-deployment", bullet "constant KV cache"); the shared table and the
+ * layer views are this library's.
+ * Through the cache handle: kv_cache_set_condition(_rows) and
+ * kv_cache_append_chunk write all layers at once (inputs [L][H][n][D]
+ * contiguous, i.e. [L*H][n][D]); kv_cache_evict / _reset / _query act on the
+ * shared table.  Attention on a cache of more than one layer goes through a
+ * layer view.  Errors: as kv_cache_create, INVALID (layers < 1).
+ */
+int kv_cache_create_layers(int chunk_tokens, int window_w, int n_sink, int cond_len, int heads,
+                           int head_dim, int kv_dtype, int layers, kvc_handle* out);
+
+/*
+ * kv_cache_layer - a handle for layer `layer` of the cache (made on the first
+ * call, owned by the cache and freed with it; kv_cache_destroy rejects it).
+ * Every attention call (sink_window_attention, _rows, _chunks, autotune and
+ * the configuration calls), kv_cache_set_condition(_rows) (this layer's
+ * condition, [H][n][D]), kv_cache_write_chunk, kv_cache_query and
+ * kv_cache_pool_view work on a view; appends, evictions and resets go
+ * through the cache (STATE otherwise).
+ * Errors: INVALID (not a cache handle, layer out of range), OOM.
+ */
+int kv_cache_layer(kvc_handle h, int layer, kvc_handle* out_view);
+
+/*
+ * kv_cache_write_chunk / kv_cache_append_commit - the append of
+ * kv_cache_append_chunk in two parts, for models that produce each layer's
+ * clean K/V in that layer: write_chunk writes the chunk about to be appended
+ * (bf16 [H][T][D] for a view, [L*H][T][D] for the cache) into the slot the
+ * next append takes, without changing the table; append_commit (on the
+ * cache) then records the chunk, as kv_cache_append_chunk does after its
+ * write.  A layer's write must follow that layer's last attention call of
+ * the current chunk: the slot may still hold the chunk being evicted, which
+ * that call sees.  Errors: INVALID, HIP; STATE (commit through a view).
+ */
+int kv_cache_write_chunk(kvc_handle h, const void* k, const void* v, void* stream);
+int kv_cache_append_commit(kvc_handle h, int64_t* out_chunk_id, int* out_slot, int64_t* out_evicted);
+
 /* Free the pool and the handle (synchronises the device first).  NULL is a no-op. */
 int kv_cache_destroy(kvc_handle h);
 
