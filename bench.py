@@ -181,6 +181,39 @@ def flatness(args) -> int:
     return 0
 
 
+def measure_peaks(stream) -> dict:
+    """Sustained rates of this device from the library's probes: bf16 MFMA
+    (v_mfma_f32_32x32x16_bf16, independent accumulators, 2 waves per SIMD) and a
+    16-byte-vector device copy of 1 GiB (read + write bytes).  Best of 3."""
+    import torch
+    from block_causal_kv_amd import _lib
+    import ctypes as C
+    lib = _lib.load()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 2 * cus, 20000
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    sp = C.c_void_p(stream.cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best_mfma, best_copy = 0.0, 0.0
+    for _ in range(3):
+        e0.record(stream)
+        _lib.check(lib.kvc_probe_mfma_bf16(C.c_void_p(sink.data_ptr()), blocks, iters, sp))
+        e1.record(stream)
+        e1.synchronize()
+        best_mfma = max(best_mfma, blocks * 4 * iters * 4 * 32768.0 / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        e0.record(stream)
+        _lib.check(lib.kvc_probe_copy(C.c_void_p(src.data_ptr()), C.c_void_p(dst.data_ptr()), src.numel(), sp))
+        e1.record(stream)
+        e1.synchronize()
+        best_copy = max(best_copy, 2.0 * src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst, sink
+    return {"bf16_mfma_tflops": round(best_mfma, 1), "hbm_copy_gbps": round(best_copy, 1),
+            "what": "library probes: %d workgroups x 4 waves x %d x 4 independent 32x32x16 bf16 MFMAs; "
+                    "1 GiB device copy (read + write bytes); best of 3" % (blocks, iters)}
+
+
 def stream_flop(spec: synthetic.StreamSpec, n: int) -> float:
     """Algorithmic FLOP of the whole-stream form over chunks 0..n-1: chunk c
     sees the condition rows, sinks 0..min(n_sink, lo)-1 and chunks lo..c,
@@ -265,6 +298,8 @@ def main() -> int:
     ap.add_argument("--flatness", action="store_true",
                     help="stream the 300-chunk long config from an empty cache and report per-chunk "
                          "latency flatness and device memory instead of the throughput line")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the MFMA and copy probes that report this device's sustained rates")
     ap.add_argument("--no-autotune", action="store_true",
                     help="keep the default launch configuration instead of timing each once before the run")
     ap.add_argument("--chunks", type=int, default=0,
@@ -386,6 +421,11 @@ def main() -> int:
                      "algorithmic_bytes_per_launch": bytes_per_call(spec),
                      "algorithmic_flop_per_launch": fl_call},
     }
+    peaks = measure_peaks(stream) if not args.no_probes else None  # after the timed region
+    if peaks is not None:
+        peaks["attention_frac_of_measured_mfma"] = round(achieved / peaks["bf16_mfma_tflops"], 4)
+        peaks["append_frac_of_measured_copy"] = round(rec["append_GBps"] / peaks["hbm_copy_gbps"], 4)
+        rec["measured_peaks"] = peaks
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(spec)
     else:

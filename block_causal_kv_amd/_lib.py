@@ -29,6 +29,8 @@ SIGNATURES = {
     "kv_cache_write_chunk": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p]),
     "kv_cache_append_commit": (C.c_int, [C.c_void_p, C.POINTER(C.c_int64), C.POINTER(C.c_int),
                                          C.POINTER(C.c_int64)]),
+    "kvc_probe_mfma_bf16": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p]),
+    "kvc_probe_copy": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
     "sink_window_attention_rows": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,
                                              C.c_void_p, C.c_void_p, C.c_float, C.c_void_p]),
     "kv_cache_set_condition_rows": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]),

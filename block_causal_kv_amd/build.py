@@ -10,8 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvc.so")
-SOURCES = ["attention_bf16.hip", "attention_fp8.hip", "quant_fp8.hip", "append.hip", "kvc_api.cpp",
-           "slot_table.cpp"]
+SOURCES = ["attention_bf16.hip", "attention_fp8.hip", "quant_fp8.hip", "append.hip", "probes.hip",
+           "kvc_api.cpp", "slot_table.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -103,4 +103,8 @@ int launch_quantize_fp8(const uint16_t* k, const uint16_t* v, int H, int rows, i
                         uint8_t* k_dst, int64_t k_head, uint8_t* vt_dst, int64_t vt_rows, int row0,
                         float* scales, int scale_tensor, int scale_head, hipStream_t stream);
 
+// Measurement probes (csrc/probes.hip).
+int launch_mfma_probe(float* sink, int blocks, int iters, hipStream_t stream);
+int launch_copy_probe(const void* src, void* dst, int64_t bytes, int num_cus, hipStream_t stream);
+
 }  // namespace kvc

@@ -270,8 +270,10 @@ int kvc_chunks_workspace_bytes(kvc_handle h, int n_chunks, size_t* out_bytes);
  *                         attention calls use.  Errors: INVALID (bad id).
  * kv_cache_autotune - run sink_window_attention on these inputs (the cache's
  *   current contents: call it at the state to tune for, e.g. a full window)
- *   with every configuration: one warm-up and `reps` timed calls each (HIP
- *   events on `stream`; the call waits for them), then keep the fastest.
+ *   with every configuration: three rounds over the configurations, each
+ *   with one warm-up and `reps` timed calls per configuration (HIP events on
+ *   `stream`; the call waits for them); a configuration's time is its best
+ *   round, and the fastest is kept.
  *   o holds that last run's output (not necessarily the chosen
  *   configuration's).  out_ms (NULL or count floats) receives the mean time
  *   per call of each configuration.  The cache's slot table is unchanged.
@@ -283,6 +285,19 @@ int kv_cache_set_config(kvc_handle h, int id);
 int kv_cache_get_config(kvc_handle h, int* out_id);
 int kv_cache_autotune(kvc_handle h, const void* q, const void* k_cur, const void* v_cur, void* o, int reps,
                       void* stream, int* out_id, float* out_ms);
+
+/*
+ * Measurement probes (not part of the method).  kvc_probe_mfma_bf16 runs
+ * `blocks` workgroups of 4 waves, each wave issuing iters x 4 independent
+ * v_mfma_f32_32x32x16_bf16 (32768 FLOP each), and writes one float per
+ * thread to the device array sink [blocks * 256]: the sustained rate of the
+ * attention kernel's MFMA on this device.  kvc_probe_copy copies `bytes`
+ * (a multiple of 16) from src to dst (device pointers) with 16-byte loads and
+ * stores.  Both are asynchronous on `stream`; the caller times them.
+ * Errors: INVALID, HIP.
+ */
+int kvc_probe_mfma_bf16(float* sink, int blocks, int iters, void* stream);
+int kvc_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 /*
  * kv_cache_pool_view - device addresses of the pool, for inspection (tests,
