@@ -114,7 +114,6 @@ template <int D, int NW, int WGS, bool STREAM>
 __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a) {
   using C = Cfg<D, NW>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::BUF_B];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -201,7 +200,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
       t0 = (int)(g - (int64_t)unit * a.tiles);
       t1 = (int)min((int64_t)a.tiles, t0 + (g_end - g));
       g += t1 - t0;
-      // every wave is done with the previous item's LDS tiles and s_last
+      // every wave is done with the previous item's LDS tiles
       if (item > 0) __syncthreads();
     }
     // stream form: visible chunks [0, ns) and [lo, chunk]; the cond rows come first
@@ -448,18 +447,13 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
       cur = nxt;
     }
 
-    // ---- a piece of a unit split between ranges: leave the partial result; the
-    // piece that finishes last merges them.  The pieces of unit u are those of
-    // ranges range_of(u0) .. range_of(u0 + tiles - 1); a range holds at most
-    // two pieces (its first item and its last), at workspace slots 2r and 2r+1,
-    // and the unit's counter is that of its last range (the only range that
-    // starts inside it).
+    // ---- a piece of a unit split between ranges: leave the partial result
+    // (unnormalised O^T, running max, partial sum) for merge_pieces_kernel.
+    // A range holds at most two pieces (its first item and its last), at
+    // workspace slots 2r and 2r+1.
     bool store = true;
     if (!STREAM && (t0 > 0 || t1 < a.tiles)) {
       constexpr int NR = C::DB * 16;  // O^T registers per lane
-      const int64_t u0 = (int64_t)unit * a.tiles - base;
-      const int r_first = range_of(u0, a.total, a.n_ranges);
-      const int r_last = range_of(u0 + a.tiles - 1, a.total, a.n_ranges);
       const int piece = 2 * r + (item == 0 ? 0 : 1);
       float* po = a.ws_o + (size_t)(piece * C::NW + wave) * NR * 64 + lane;
       float* pml = a.ws_ml + (size_t)(piece * C::NW + wave) * 2 * 64 + lane;
@@ -469,31 +463,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
         for (int k = 0; k < 16; ++k) po[(db * 16 + k) * 64] = oacc[db][k];
       pml[0] = m_run;
       pml[64] = l_run;
-      __threadfence();  // publish the partial before counting this piece done
-      __syncthreads();
-      if (tid == 0) s_last = atomicAdd(&a.ws_cnt[r_last], 1) == r_last - r_first;
-      __syncthreads();
-      store = s_last;
-      if (store) {
-        __threadfence();  // see every other piece's partial
-        for (int j = r_first; j <= r_last; ++j) {
-          if (j == r) continue;
-          const int slot = (base + range_lo(j, a.total, a.n_ranges)) / a.tiles == unit ? 0 : 1;
-          const size_t pj = (size_t)(2 * j + slot) * C::NW + wave;
-          const float* qo = a.ws_o + pj * NR * 64 + lane;
-          const float* qml = a.ws_ml + pj * 2 * 64 + lane;
-          const float mj = qml[0], lj = qml[64];
-          const float mm = fmaxf(m_run, mj);
-          const float a0 = __builtin_amdgcn_exp2f(m_run - mm), a1 = __builtin_amdgcn_exp2f(mj - mm);
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-            for (int k = 0; k < 16; ++k) oacc[db][k] = oacc[db][k] * a0 + qo[(db * 16 + k) * 64] * a1;
-          l_run = l_run * a0 + lj * a1;
-          m_run = mm;
-        }
-        if (tid == 0) a.ws_cnt[r_last] = 0;  // ready for the next call
-      }
+      store = false;
     }
 
     // ---- epilogue: O = O^T / l, bf16; lane holds dims db*32 + 8*(k/4) + 4*hf + k%4
@@ -517,6 +487,62 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
       }
     }
   }
+}
+
+// Merge of the units split between ranges: one workgroup per unit of the
+// last round (units cut by no range boundary return at once), one wave per
+// 32-row block, each lane one query row half as in the attention kernel.  It
+// runs after the attention kernel on the same stream, so the partials are
+// visible without fences; pieces are merged in range order (deterministic).
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void merge_pieces_kernel(AttnArgs a) {
+  using C = Cfg<D, NW>;
+  constexpr int NR = C::DB * 16;
+  const int unit = a.n_whole + blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int hf = lane >> 5, col = lane & 31;
+  const int64_t base = (int64_t)a.n_whole * a.tiles;
+  const int64_t u0 = (int64_t)unit * a.tiles - base;
+  const int r_first = range_of(u0, a.total, a.n_ranges);
+  const int r_last = range_of(u0 + a.tiles - 1, a.total, a.n_ranges);
+  if (r_first == r_last) return;  // the unit was computed whole
+  const int head = unit / a.q_tiles, qtile = unit % a.q_tiles;
+  const int row_beg = qtile * a.q_rows;
+  const int row_end = min(a.Tq, row_beg + a.q_rows);
+  if (row_beg + wave * 32 >= row_end) return;  // (wave-uniform) no rows
+  const int qrow = row_beg + wave * 32 + col;
+  float o[NR];
+#pragma unroll
+  for (int k = 0; k < NR; ++k) o[k] = 0.f;
+  float m = kNegInf, l = 0.f;
+  for (int j = r_first; j <= r_last; ++j) {
+    const int slot = (base + range_lo(j, a.total, a.n_ranges)) / a.tiles == unit ? 0 : 1;
+    const size_t pj = (size_t)(2 * j + slot) * NW + wave;
+    const float* qo = a.ws_o + pj * NR * 64 + lane;
+    const float* qml = a.ws_ml + pj * 2 * 64 + lane;
+    const float mj = qml[0], lj = qml[64];
+    const float mm = fmaxf(m, mj);
+    const float a0 = __builtin_amdgcn_exp2f(m - mm), a1 = __builtin_amdgcn_exp2f(mj - mm);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) o[k] = o[k] * a0 + qo[k * 64] * a1;
+    l = l * a0 + lj * a1;
+    m = mm;
+  }
+  const float l_tot = sum_halves(l);
+  if (qrow >= row_end) return;
+  const float inv = 1.f / l_tot;
+  uint16_t* dst = a.o + ((int64_t)head * a.Tq + qrow) * D + 4 * hf;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float* v = o + db * 16 + 4 * q4;
+      const uint32_t w0 = (uint32_t)f2bf(v[0] * inv) | ((uint32_t)f2bf(v[1] * inv) << 16);
+      const uint32_t w1 = (uint32_t)f2bf(v[2] * inv) | ((uint32_t)f2bf(v[3] * inv) << 16);
+      *(uint2*)(dst + db * 32 + 8 * q4) = make_uint2(w0, w1);
+    }
+  if (a.lse != nullptr && hf == 0)
+    a.lse[(int64_t)head * a.Tq + qrow] = (m + __log2f(l_tot)) * 0.69314718055994530942f;
 }
 
 // Launch configurations: waves per workgroup x workgroups resident per CU
@@ -568,13 +594,21 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
       if (n_ranges > total) n_ranges = total >= 8 ? (int)(total & ~(int64_t)7) : (int)total;
     }
   }
+  // the workspace holds two pieces (and one counter) per workgroup slot
+  if (n_ranges > slots) return -2;
   a.n_whole = units - rest;
   a.total = (int64_t)rest * tiles;
   a.n_ranges = n_ranges;
   a.grid_whole = 8 * ((a.n_whole + 7) / 8);
   const int grid = a.grid_whole + 8 * ((a.n_ranges + 7) / 8);
   hipLaunchKernelGGL((attention_bf16_kernel<D, NW, WGS, false>), dim3(grid), dim3(C::NT), 0, stream, a);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  if (hipGetLastError() != hipSuccess) return -1;
+  // ranges that are not exactly the last round's units split some of them
+  if (n_ranges > 0 && n_ranges != rest) {
+    hipLaunchKernelGGL((merge_pieces_kernel<D, NW>), dim3(rest), dim3(C::NT), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return -1;
+  }
+  return 0;
 }
 
 template <int D, int NW, int WGS>
