@@ -26,7 +26,8 @@
 // starts and lengths are multiples of 16 rows.  Schedule as in the bf16
 // kernel: one 8-wave workgroup per CU and (head, query tile of up to 256
 // rows), 64-key tiles loaded straight into double-buffered LDS (buffer_load
-// ... lds, spread over the S^T MFMAs), key-slice split of the last round.
+// ... lds, spread over the S^T MFMAs), key-slice split of the last round
+// (slices leave partials that a second kernel merges).
 //
 // Key order: K rows are read so that in S^T's accumulator lane half hf holds
 // keys kb*32 + 16*hf + r in register r (16 consecutive keys per 32-key
@@ -84,7 +85,6 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
   using C = F8Cfg<D>;
   constexpr int BN = C::BN;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::BUF_B];
-  __shared__ int s_last;
   __shared__ float s_ks[kMaxSegments], s_lv[kMaxSegments];  // per segment: K scale, log2(V scale / vs_ref)
 
   int unit, t0 = 0, t1 = a.tiles, piece = -1, ru = 0;
@@ -394,8 +394,8 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
     cur = nxt;
   }
 
-  // ---- a slice of a split unit: leave the partial result; the last slice merges
-  // (every slice of a unit uses the same vs_ref, so the partials add directly)
+  // ---- a slice of a split unit: leave the partial result, scaled by vs_ref
+  // (every slice of a unit uses the same vs_ref), for merge_slices_kernel
   if (piece >= 0) {
     constexpr int NR = C::DB * 16;
     float* po = a.ws_o + (size_t)(piece * C::NW + wave) * NR * 64 + lane;
@@ -403,32 +403,10 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) po[(db * 16 + r) * 64] = oacc[db][r];
+      for (int r = 0; r < 16; ++r) po[(db * 16 + r) * 64] = oacc[db][r] * vs_ref;
     pml[0] = m_run;
     pml[64] = l_run;
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&a.ws_cnt[ru], 1) == a.slices - 1;
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const int my_slice = piece / a.rest;
-    for (int j = 0; j < a.slices; ++j) {
-      if (j == my_slice) continue;
-      const size_t pj = (size_t)(j * a.rest + ru) * C::NW + wave;
-      const float* qo = a.ws_o + pj * NR * 64 + lane;
-      const float* qml = a.ws_ml + pj * 2 * 64 + lane;
-      const float mj = qml[0], lj = qml[64];
-      const float mm = fmaxf(m_run, mj);
-      const float a0 = __builtin_amdgcn_exp2f(m_run - mm), a1 = __builtin_amdgcn_exp2f(mj - mm);
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a0 + qo[(db * 16 + r) * 64] * a1;
-      l_run = l_run * a0 + lj * a1;
-      m_run = mm;
-    }
-    if (tid == 0) a.ws_cnt[ru] = 0;
+    return;
   }
 
   // ---- epilogue: O = vs_ref * O^T / l
@@ -446,6 +424,55 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
       }
     if (a.lse != nullptr && hf == 0) a.lse[head_rows + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
   }
+}
+
+// Merge of the split units: one workgroup per unit of the last round, one
+// wave per 32-row block; launched after the attention kernel on the same
+// stream (the kernel boundary orders the partials).  Slices merge in order.
+template <int D>
+__global__ __launch_bounds__(F8Cfg<D>::NT) void merge_slices_kernel(AttnArgs a) {
+  using C = F8Cfg<D>;
+  constexpr int NR = C::DB * 16;
+  const int ru = blockIdx.x;
+  const int unit = a.n_whole + ru;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int hf = lane >> 5, col = lane & 31;
+  const int head = unit / a.q_tiles, qtile = unit % a.q_tiles;
+  const int row_beg = qtile * a.q_rows;
+  const int row_end = min(a.Tq, row_beg + a.q_rows);
+  if (row_beg + wave * 32 >= row_end) return;  // (wave-uniform) no rows
+  const int qrow = row_beg + wave * 32 + col;
+  float o[NR];
+#pragma unroll
+  for (int k = 0; k < NR; ++k) o[k] = 0.f;
+  float m = kNegInf, l = 0.f;
+  for (int j = 0; j < a.slices; ++j) {
+    const size_t pj = (size_t)(j * a.rest + ru) * C::NW + wave;
+    const float* qo = a.ws_o + pj * NR * 64 + lane;
+    const float* qml = a.ws_ml + pj * 2 * 64 + lane;
+    const float mj = qml[0], lj = qml[64];
+    const float mm = fmaxf(m, mj);
+    const float a0 = __builtin_amdgcn_exp2f(m - mm), a1 = __builtin_amdgcn_exp2f(mj - mm);
+#pragma unroll
+    for (int k = 0; k < NR; ++k) o[k] = o[k] * a0 + qo[k * 64] * a1;
+    l = l * a0 + lj * a1;
+    m = mm;
+  }
+  const float l_tot = sum_halves(l);
+  if (qrow >= row_end) return;
+  const float f = 1.f / l_tot;
+  uint16_t* dst = a.o + ((int64_t)head * a.Tq + qrow) * D + 4 * hf;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float* v = o + db * 16 + 4 * g;
+      const uint32_t w0 = (uint32_t)f2bf(v[0] * f) | ((uint32_t)f2bf(v[1] * f) << 16);
+      const uint32_t w1 = (uint32_t)f2bf(v[2] * f) | ((uint32_t)f2bf(v[3] * f) << 16);
+      *(uint2*)(dst + db * 32 + 8 * g) = make_uint2(w0, w1);
+    }
+  if (a.lse != nullptr && hf == 0)
+    a.lse[(int64_t)head * a.Tq + qrow] = (m + __log2f(l_tot)) * 0.69314718055994530942f;
 }
 
 constexpr int kMaxSlicesF8 = 8;
@@ -484,7 +511,12 @@ int launch_fp8(AttnArgs& a, hipStream_t stream) {
   a.grid_whole = 8 * ((a.n_whole + 7) / 8);
   const int grid = a.grid_whole + 8 * ((a.rest * a.slices + 7) / 8);
   hipLaunchKernelGGL((attention_fp8_kernel<D>), dim3(grid), dim3(C::NT), 0, stream, a);
-  return hipGetLastError() == hipSuccess ? 0 : -1;
+  if (hipGetLastError() != hipSuccess) return -1;
+  if (a.slices > 1) {
+    hipLaunchKernelGGL((merge_slices_kernel<D>), dim3(a.rest), dim3(C::NT), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return -1;
+  }
+  return 0;
 }
 
 }  // namespace
