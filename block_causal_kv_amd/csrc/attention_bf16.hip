@@ -574,17 +574,18 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
   //             same K/V in step (slice k of each);
   //  unaligned: n_ranges = slots: equal work per slot, but ranges start at
   //             arbitrary key offsets and every workgroup fetches its own K/V
-  //             stream past L2 (measured about 1.35x slower per tile at
+  //             stream past L2 (measured about 1.25x slower per tile at
   //             720p-sized K/V).
   // A last round that is nearly full is run whole instead.  Costs are in units
-  // of one whole-unit round; a split pays a small merge cost per slice.
+  // of one whole-unit round; a split pays a small merge cost per slice (the
+  // merge kernel reads one more partial per slice).
   const int slots = WGS * a.num_cus;
   int rest = a.ws_o == nullptr ? 0 : units % slots;
   int n_ranges = 0;
   if (rest > 0) {
     const int s = slots / rest;
-    const double aligned = 1.0 / s + (s > 1 ? 0.02 * s : 0.0);
-    const double unaligned = 1.35 * rest / slots + 0.04;
+    const double aligned = 1.0 / s + (s > 1 ? 0.005 * s : 0.0);
+    const double unaligned = 1.25 * rest / slots + 0.01;
     const double whole = units > slots ? 1.0 : 1e30;  // (only when other rounds exist)
     if (whole <= aligned && whole <= unaligned) {
       rest = 0;
