@@ -64,9 +64,10 @@ def kernel_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(config: str):
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
+def measured_traffic(config: str, launch_config: int):
+    """HBM bytes per attention launch of the given launch configuration from
+    the committed rocprofv3 counter summary, if it was taken on the current
+    kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -74,7 +75,8 @@ def measured_traffic(config: str):
         return None
     if t.get("kernel_sha") != kernel_sha() or t.get("config") != config:
         return None
-    return t.get("hbm_bytes_per_launch")
+    e = t.get("by_launch_config", {}).get(str(launch_config))
+    return None if e is None else e.get("hbm_bytes_per_launch")
 
 
 def cpu_baseline(spec: synthetic.StreamSpec, budget_s: float = 12.0) -> dict:
@@ -392,7 +394,7 @@ def main() -> int:
     attn_avg = float(np.mean(attn_ms))
     achieved = fl_call / (attn_avg * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if spec.kv_dtype == "fp8" else PEAK_BF16_TFLOPS
-    traffic = measured_traffic(args.config)
+    traffic = measured_traffic(args.config, cache.config) if spec.kv_dtype == "bf16" else None
     app_bytes = 2.0 * 2 * H * T * D * (1 if spec.kv_dtype == "fp8" else 2)  # K+V read and written
     rec = {
         "metric": METRIC,

@@ -534,12 +534,14 @@ int kv_cache_autotune(kvc_handle h, const void* q, const void* k_cur, const void
       if (round == 0 || ms < ms_best[id]) ms_best[id] = ms;
     }
   }
+  // the default (configuration 0) is kept unless another is at least 2 %
+  // faster: closer timings are within the run-to-run noise of one box
   int best = before;
   if (rc == KVC_OK) {
     best = 0;
     for (int id = 0; id < n; ++id) {
       if (out_ms) out_ms[id] = ms_best[id];
-      if (ms_best[id] < ms_best[best]) best = id;
+      if (ms_best[id] < ms_best[best] * (best == 0 ? 0.98f : 1.f)) best = id;
     }
   }
   (void)hipEventDestroy(e0);

@@ -273,7 +273,8 @@ int kvc_chunks_workspace_bytes(kvc_handle h, int n_chunks, size_t* out_bytes);
  *   with every configuration: three rounds over the configurations, each
  *   with one warm-up and `reps` timed calls per configuration (HIP events on
  *   `stream`; the call waits for them); a configuration's time is its best
- *   round, and the fastest is kept.
+ *   round, and the fastest is kept, except that configuration 0 stays unless
+ *   another is at least 2 % faster.
  *   o holds that last run's output (not necessarily the chosen
  *   configuration's).  out_ms (NULL or count floats) receives the mean time
  *   per call of each configuration.  The cache's slot table is unchanged.

@@ -56,7 +56,7 @@ def test_config_table_and_autotune():
     best, ms = cache.autotune(q, k, v, reps=3)
     say("autotune: config %d, ms %s" % (best, ms))
     assert 0 <= best < 3 and len(ms) == 3 and all(m > 0 for m in ms)
-    assert ms[best] == min(ms)
+    assert ms[best] == min(ms) or (best == 0 and min(ms) >= 0.98 * ms[0])
     assert cache.config == best
     assert cache.query() == before
     # every configuration gives the same result up to rounding order
