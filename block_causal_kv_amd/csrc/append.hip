@@ -28,29 +28,37 @@ __global__ __launch_bounds__(256) void rows_copy_kernel(const uint4* __restrict_
 }
 
 // One block: 64 rows of one chunk of one head (grid: row tiles x H x chunks).
-// Rows past `rows` read as zero, so the last 8-column piece is completed with
-// zeros.
+// Each thread loads two consecutive rows' 16-byte pieces of one 8-dim group
+// and joins them per dim into 32-bit words (row 2i in the low half, 2i+1 in
+// the high half), so the LDS tile is written in 32-bit words; consecutive
+// threads take consecutive row pairs, which keeps those writes free of bank
+// conflicts.  Rows past `rows` read as zero, so the last 8-column piece is
+// completed with zeros.
 template <int D>
 __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t* __restrict__ src,
                                                           uint16_t* __restrict__ vt, int rows, int64_t vt_rows,
                                                           int col0, int col_stride) {
   constexpr int TR = 64;
-  constexpr int STR = TR + 8;  // LDS row stride (elements) of the transposed tile
-  __shared__ __attribute__((aligned(16))) uint16_t tile[D * STR];
+  constexpr int STR = TR / 2 + 4;  // 32-bit words per dim row of the tile (row pairs + padding)
+  __shared__ __attribute__((aligned(16))) uint32_t tile[D * STR];
   const int h = blockIdx.y;
   const int ch = blockIdx.z;
   const int r0 = blockIdx.x * TR;
   const uint16_t* s = src + (((int64_t)h * gridDim.z + ch) * rows + r0) * D;
   col0 += ch * col_stride;
   constexpr int CH = D / 8;  // 16-byte pieces per input row
-  for (int idx = threadIdx.x; idx < TR * CH; idx += blockDim.x) {
-    const int r = idx / CH, c8 = idx % CH;
-    const uint4 w = r0 + r < rows ? *(const uint4*)(s + (int64_t)r * D + c8 * 8) : make_uint4(0, 0, 0, 0);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  for (int idx = threadIdx.x; idx < (TR / 2) * CH; idx += blockDim.x) {
+    const int rp = idx % (TR / 2), c8 = idx / (TR / 2);
+    const int r = 2 * rp;
+    const uint4 w0 = r0 + r < rows ? *(const uint4*)(s + (int64_t)r * D + c8 * 8) : make_uint4(0, 0, 0, 0);
+    const uint4 w1 = r0 + r + 1 < rows ? *(const uint4*)(s + (int64_t)(r + 1) * D + c8 * 8) : make_uint4(0, 0, 0, 0);
+    const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w};
+    const uint32_t b[4] = {w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      tile[(c8 * 8 + 2 * j) * STR + r] = (uint16_t)(ws[j] & 0xFFFFu);
-      tile[(c8 * 8 + 2 * j + 1) * STR + r] = (uint16_t)(ws[j] >> 16);
+      // dim 2j: low halves of both rows; dim 2j + 1: high halves
+      tile[(c8 * 8 + 2 * j) * STR + rp] = __builtin_amdgcn_perm(b[j], a[j], 0x05040100u);
+      tile[(c8 * 8 + 2 * j + 1) * STR + rp] = __builtin_amdgcn_perm(b[j], a[j], 0x07060302u);
     }
   }
   __syncthreads();
@@ -59,7 +67,7 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t* __rest
   for (int idx = threadIdx.x; idx < D * (TR / 8); idx += blockDim.x) {
     const int d = idx / (TR / 8), p = idx % (TR / 8);
     if (p >= npieces) continue;
-    const uint4 w = *(const uint4*)(&tile[d * STR + 8 * p]);
+    const uint4 w = *(const uint4*)(&tile[d * STR + 4 * p]);
     *(uint4*)(vt + ((int64_t)h * D + d) * vt_rows + col0 + r0 + 8 * p) = w;
   }
 }

@@ -489,17 +489,18 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
   }
 }
 
-// Merge of the units split between ranges: one workgroup per unit of the
-// last round (units cut by no range boundary return at once), one wave per
-// 32-row block, each lane one query row half as in the attention kernel.  It
-// runs after the attention kernel on the same stream, so the partials are
-// visible without fences; pieces are merged in range order (deterministic).
+// Merge of the units split between ranges: one single-wave workgroup per
+// (unit of the last round, 32-row block), so the merge spreads over the CUs
+// (units cut by no range boundary return at once); each lane one query row
+// half as in the attention kernel.  It runs after the attention kernel on
+// the same stream, so the partials are visible without fences; pieces are
+// merged in range order (deterministic).
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void merge_pieces_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64) void merge_pieces_kernel(AttnArgs a) {
   using C = Cfg<D, NW>;
   constexpr int NR = C::DB * 16;
-  const int unit = a.n_whole + blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int unit = a.n_whole + (int)(blockIdx.x / NW);
+  const int wave = (int)(blockIdx.x % NW), lane = threadIdx.x;
   const int hf = lane >> 5, col = lane & 31;
   const int64_t base = (int64_t)a.n_whole * a.tiles;
   const int64_t u0 = (int64_t)unit * a.tiles - base;
@@ -606,7 +607,7 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
   if (hipGetLastError() != hipSuccess) return -1;
   // ranges that are not exactly the last round's units split some of them
   if (n_ranges > 0 && n_ranges != rest) {
-    hipLaunchKernelGGL((merge_pieces_kernel<D, NW>), dim3(rest), dim3(C::NT), 0, stream, a);
+    hipLaunchKernelGGL((merge_pieces_kernel<D, NW>), dim3(rest * NW), dim3(64), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return -1;
   }
   return 0;

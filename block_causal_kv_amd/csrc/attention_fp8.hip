@@ -426,16 +426,16 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
   }
 }
 
-// Merge of the split units: one workgroup per unit of the last round, one
-// wave per 32-row block; launched after the attention kernel on the same
+// Merge of the split units: one single-wave workgroup per (unit of the last
+// round, 32-row block); launched after the attention kernel on the same
 // stream (the kernel boundary orders the partials).  Slices merge in order.
 template <int D>
-__global__ __launch_bounds__(F8Cfg<D>::NT) void merge_slices_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64) void merge_slices_kernel(AttnArgs a) {
   using C = F8Cfg<D>;
   constexpr int NR = C::DB * 16;
-  const int ru = blockIdx.x;
+  const int ru = (int)(blockIdx.x / C::NW);
   const int unit = a.n_whole + ru;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = (int)(blockIdx.x % C::NW), lane = threadIdx.x;
   const int hf = lane >> 5, col = lane & 31;
   const int head = unit / a.q_tiles, qtile = unit % a.q_tiles;
   const int row_beg = qtile * a.q_rows;
@@ -513,7 +513,7 @@ int launch_fp8(AttnArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((attention_fp8_kernel<D>), dim3(grid), dim3(C::NT), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return -1;
   if (a.slices > 1) {
-    hipLaunchKernelGGL((merge_slices_kernel<D>), dim3(a.rest), dim3(C::NT), 0, stream, a);
+    hipLaunchKernelGGL((merge_slices_kernel<D>), dim3(a.rest * C::NW), dim3(64), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return -1;
   }
   return 0;
