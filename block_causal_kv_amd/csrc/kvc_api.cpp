@@ -51,7 +51,8 @@ struct kvc_cache {
   size_t k_bytes = 0, v_bytes = 0;
   float* scales = nullptr;    // fp8: [2][L*H][blocks]: block 0 = condition, 1 + s = slot s, last = current
   int scale_tensor = 0;       // fp8: L * H * blocks (offset of the V scales)
-  uint32_t* amax = nullptr;   // fp8: [2][L*H] scratch of the quantiser
+  uint32_t* amax = nullptr;   // fp8: scratch of the quantiser, two buffers [2][L*H] used in turn
+  int amax_turn = 0;          // fp8 (root): the buffer the next quantisation uses (zeroed)
   int blocks() const { return n_sink + W + 2; }
   int num_cus = 0;
   float* ws_o = nullptr;   // attention workspace: partials of split query tiles
@@ -87,9 +88,16 @@ namespace {
 
 // fp8 cache: quantise K/V bf16 [H][rows][D] into pool rows [row0, row0 + rows) with scale block blk.
 int quantize_into(kvc_cache* h, const void* k, const void* v, int rows, int row0, int blk, hipStream_t st) {
-  return kvc::launch_quantize_fp8((const uint16_t*)k, (const uint16_t*)v, h->heads_written(), rows, h->D,
-                                  h->amax, (uint8_t*)h->k_pool, h->spare_rows * h->D, (uint8_t*)h->v_pool,
-                                  h->spare_rows, row0, h->scales + blk, h->scale_tensor, h->blocks(), st);
+  kvc_cache* r = h->top();
+  const int n = 2 * r->H * r->layers;  // words of one amax buffer
+  uint32_t* cur = r->amax + (size_t)r->amax_turn * n;
+  uint32_t* next = r->amax + (size_t)(1 - r->amax_turn) * n;
+  const int rc = kvc::launch_quantize_fp8((const uint16_t*)k, (const uint16_t*)v, h->heads_written(), rows, h->D,
+                                          cur, next, n, (uint8_t*)h->k_pool, h->spare_rows * h->D,
+                                          (uint8_t*)h->v_pool, h->spare_rows, row0, h->scales + blk,
+                                          h->scale_tensor, h->blocks(), st);
+  if (rc == 0) r->amax_turn = 1 - r->amax_turn;
+  return rc;
 }
 
 // bf16 cache: K rows copied to pool rows [row0, row0 + rows), V written transposed to columns row0...
@@ -183,7 +191,8 @@ int kv_cache_create_layers(int chunk_tokens, int window_w, int n_sink, int cond_
   e = hipMalloc(&c->k_pool, c->k_bytes);
   if (e == hipSuccess) e = hipMalloc(&c->v_pool, c->v_bytes);
   if (e == hipSuccess && fp8) e = hipMalloc(&c->scales, sizeof(float) * 2 * all_heads * c->blocks());
-  if (e == hipSuccess && fp8) e = hipMalloc(&c->amax, sizeof(uint32_t) * 2 * all_heads);
+  if (e == hipSuccess && fp8) e = hipMalloc(&c->amax, sizeof(uint32_t) * 4 * all_heads);
+  if (e == hipSuccess && fp8) e = hipMemset(c->amax, 0, sizeof(uint32_t) * 4 * all_heads);
   if (e == hipSuccess && fp8) e = hipMemset(c->scales, 0, sizeof(float) * 2 * all_heads * c->blocks());
   const int n_cnt = kvc::attention_ws_counters(c->num_cus);
   if (e == hipSuccess) e = hipMalloc(&c->ws_o, kvc::attention_ws_o_bytes(c->num_cus, head_dim));

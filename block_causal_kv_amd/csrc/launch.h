@@ -99,9 +99,12 @@ int launch_attention_fp8(AttnArgs& a, int head_dim, hipStream_t stream);
 // k_dst[h*k_head + (row0 + r)*D + d], V transposed into vt_dst[(h*D + d)*vt_rows + row0 + r];
 // scales[t*scale_tensor + h*scale_head] <- amax/448 (t = 0 K, 1 V).  amax_bits:
 // 2*H words of scratch.
+// amax_bits: zeroed [2][H] scratch for this call; amax_next: the other buffer
+// ([n_amax] words), cleared here for the next call.
 int launch_quantize_fp8(const uint16_t* k, const uint16_t* v, int H, int rows, int D, uint32_t* amax_bits,
-                        uint8_t* k_dst, int64_t k_head, uint8_t* vt_dst, int64_t vt_rows, int row0,
-                        float* scales, int scale_tensor, int scale_head, hipStream_t stream);
+                        uint32_t* amax_next, int n_amax, uint8_t* k_dst, int64_t k_head, uint8_t* vt_dst,
+                        int64_t vt_rows, int row0, float* scales, int scale_tensor, int scale_head,
+                        hipStream_t stream);
 
 // Measurement probes (csrc/probes.hip).
 int launch_mfma_probe(float* sink, int blocks, int iters, hipStream_t stream);

@@ -12,7 +12,8 @@
 // [H][D][rows] (the PV product reads V^T, and the transposition is free here).
 // Two kernels: a per-head absolute maximum (atomic max on the float's bits,
 // which order like the values for non-negative floats), then the quantising
-// write, which also records the scale.
+// write, which also records the scale.  The maxima live in one of two
+// buffers used in turn; each quantisation clears the other one for the next.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,17 +49,13 @@ __device__ __forceinline__ uint32_t e4m3_rne(float y) {
   return sign | mag;
 }
 
-__global__ void zero_words_kernel(uint32_t* p, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
-}
-
 // amax of K (tensor 0) and V (tensor 1) per head: grid (blocks, H, 2).
 __global__ __launch_bounds__(256) void amax_bf16_kernel(const uint16_t* __restrict__ k,
                                                         const uint16_t* __restrict__ v, int64_t per_head,
                                                         uint32_t* __restrict__ amax_bits) {
   const uint16_t* src = (blockIdx.z == 0 ? k : v) + (int64_t)blockIdx.y * per_head;
   float m = 0.f;
+#pragma unroll 4
   for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < per_head;
        i += (int64_t)gridDim.x * blockDim.x * 8) {
     const uint4 w = *(const uint4*)(src + i);  // per_head is a multiple of 8 (D in {64, 128})
@@ -89,8 +86,12 @@ __global__ __launch_bounds__(256) void quantize_bf16_kernel(const uint16_t* __re
                                                             uint8_t* __restrict__ k_dst, int64_t k_head,
                                                             uint8_t* __restrict__ vt_dst, int64_t vt_rows,
                                                             int row0, float* __restrict__ scales,
-                                                            int scale_tensor, int scale_head) {
+                                                            int scale_tensor, int scale_head,
+                                                            uint32_t* __restrict__ amax_next, int n_next) {
   constexpr int TR = 64;  // rows per block
+  // the other amax buffer, used by the next quantisation, starts at zero
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int i = threadIdx.x; i < n_next; i += blockDim.x) amax_next[i] = 0u;
   __shared__ uint8_t tile[D][TR + 16];
   const int tensor = blockIdx.z;
   const int h = blockIdx.y;
@@ -139,10 +140,10 @@ __global__ __launch_bounds__(256) void quantize_bf16_kernel(const uint16_t* __re
 }  // namespace
 
 int launch_quantize_fp8(const uint16_t* k, const uint16_t* v, int H, int rows, int D, uint32_t* amax_bits,
-                        uint8_t* k_dst, int64_t k_head, uint8_t* vt_dst, int64_t vt_rows, int row0,
-                        float* scales, int scale_tensor, int scale_head, hipStream_t stream) {
+                        uint32_t* amax_next, int n_amax, uint8_t* k_dst, int64_t k_head, uint8_t* vt_dst,
+                        int64_t vt_rows, int row0, float* scales, int scale_tensor, int scale_head,
+                        hipStream_t stream) {
   if (rows <= 0) return 0;
-  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, stream, amax_bits, 2 * H);
   const int64_t per_head = (int64_t)rows * D;
   int blocks = (int)((per_head / 8 + 255) / 256);
   if (blocks > 64) blocks = 64;
@@ -150,10 +151,10 @@ int launch_quantize_fp8(const uint16_t* k, const uint16_t* v, int H, int rows, i
   const dim3 grid((rows + 63) / 64, H, 2);
   if (D == 128)
     hipLaunchKernelGGL(quantize_bf16_kernel<128>, grid, dim3(256), 0, stream, k, v, rows, amax_bits, k_dst,
-                       k_head, vt_dst, vt_rows, row0, scales, scale_tensor, scale_head);
+                       k_head, vt_dst, vt_rows, row0, scales, scale_tensor, scale_head, amax_next, n_amax);
   else if (D == 64)
     hipLaunchKernelGGL(quantize_bf16_kernel<64>, grid, dim3(256), 0, stream, k, v, rows, amax_bits, k_dst,
-                       k_head, vt_dst, vt_rows, row0, scales, scale_tensor, scale_head);
+                       k_head, vt_dst, vt_rows, row0, scales, scale_tensor, scale_head, amax_next, n_amax);
   else
     return -2;
   return hipGetLastError() == hipSuccess ? 0 : -1;

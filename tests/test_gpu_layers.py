@@ -174,3 +174,31 @@ def test_appends_on_a_second_stream():
                    "two streams chunk %d step %d" % (c, s))
         clean_k[c], clean_v[c] = x.k_clean, x.v_clean
     cache.close()
+
+
+def test_whole_stream_on_a_layer_view():
+    """sink_window_attention_chunks through a layer view reads that layer's
+    condition rows (each layer's condition differs)."""
+    import torch
+    from block_causal_kv_amd import KVCache
+    from oracle.mask import full_stream_mask
+    from oracle.attention import masked_attention
+    L, T, Lc, H, D, W, n = 3, 48, 16, 2, 64, 2, 5
+    specs = [synthetic.small_spec("lv%d" % l, n_chunks=n, chunk_tokens=T, cond_len=Lc, heads=H, head_dim=D,
+                                  window=W, seed=95 + l) for l in range(L)]
+    cache = KVCache(T, W, 1, Lc, H, D, layers=L)
+    conds = [synthetic.cond_inputs(sp) for sp in specs]
+    cache.set_condition(to_dev(np.concatenate([c[0] for c in conds])), to_dev(np.concatenate([c[1] for c in conds])))
+    cat = lambda xs: np.concatenate(xs, axis=1)
+    for l in (2, 0):
+        xs = [synthetic.chunk_inputs(specs[l], c) for c in range(n)]
+        qs, ks, vs = [x.q[0] for x in xs], [x.k[0] for x in xs], [x.v[0] for x in xs]
+        view = cache.layer(l)
+        view.config = 2  # the 4 x 3 configuration of D = 64
+        lse = torch.empty((H, n * T), dtype=torch.float32, device="cuda")
+        o = view.attention_chunks(to_dev(cat(qs)), to_dev(cat(ks)), to_dev(cat(vs)), lse=lse)
+        torch.cuda.synchronize()
+        m = full_stream_mask(n, T, Lc, W, 1)
+        ref, ref_lse = masked_attention(cat(qs), cat([conds[l][0]] + ks), cat([conds[l][1]] + vs), m, specs[l].scale)
+        _check(from_dev(o), lse.cpu().numpy().astype(np.float64), ref, ref_lse, False, "layer %d whole stream" % l)
+    cache.close()
