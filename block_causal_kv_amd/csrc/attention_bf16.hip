@@ -372,10 +372,12 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
           for (int k = 0; k < 16; ++k) oacc[db][k] *= alpha;
       }
       // P = exp2(s*c - m) as bf16; the row sum adds the same bf16 values that
-      // enter the PV product.
+      // enter the PV product.  Block by 32-key block: the PV MFMAs of block kb
+      // are issued before the exponentials of block kb+1, which do not depend
+      // on them, so the wave's own VALU work runs beside its MFMAs.
       float rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           unsigned w[4];
@@ -390,16 +392,17 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
           const u32x4 wv = {w[0], w[1], w[2], w[3]};
           pb[kb][h2] = __builtin_bit_cast(bf16x8, wv);
         }
+        // ---- O^T += V^T . P^T for this block's 32 keys
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            const uint4 raw = *(const uint4*)(kl + vaddr[2 * kb + h2] + db * 32 * C::VRB);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw), pb[kb][h2],
+                                                                oacc[db], 0, 0, 0);
+          }
+      }
       l_run += rs;
-      // ---- O^T += V^T . P^T
-#pragma unroll
-      for (int ks = 0; ks < C::BN / 16; ++ks)
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const uint4 raw = *(const uint4*)(kl + vaddr[ks] + db * 32 * C::VRB);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, raw),
-                                                              pb[ks >> 1][ks & 1], oacc[db], 0, 0, 0);
-        }
     };
 
     // ---- main loop over key tiles [t0, t1), unrolled by two so each half reads
