@@ -109,3 +109,15 @@ def test_evicted_nonfinite_chunk_does_not_leak():
     say("  non-finite neighbour: max_abs %.3e rel_l2 %.3e" % (ma, rl))
     assert ma <= BF16_MAX_ABS and rl <= BF16_REL_L2
     cache.close()
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_wide_window_fragmented_by_evictions(kv_dtype):
+    """W = 20 and two sinks, manual evictions leaving holes in the slot ring:
+    many key segments (fp8: one per chunk), each ending in a partial tile
+    (T = 48)."""
+    spec = synthetic.small_spec("frag_" + kv_dtype, n_chunks=34, chunk_tokens=48, cond_len=16, heads=2,
+                                head_dim=128, window=20, n_sink=2, seed=18, outlier_frac=0.01,
+                                kv_dtype=kv_dtype)
+    say("fragmented wide window", spec)
+    run_stream(spec, [5, 12, 21, 22, 27, 33], evict_plan={8: 3, 14: 5, 23: 7, 30: 2})
