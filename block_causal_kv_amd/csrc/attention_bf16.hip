@@ -40,10 +40,10 @@
 //   (unit, key tile) space that is cut into equal contiguous ranges: either
 //   each unit into the same s slices (the query tiles of a head stay in step)
 //   or one range per slot (equal work, but unaligned).  A workgroup computes
-//   the pieces of the units its range covers in turn, and a unit cut by a
-//   range boundary is finished by the piece that ends last, which merges the
-//   others' unnormalised O^T, running max and partial sums from a workspace
-//   (device-scope counter, no waiting).
+//   the pieces of the units its range covers in turn; a unit cut by a range
+//   boundary leaves the pieces' unnormalised O^T, running max and partial
+//   sums in a workspace, and a second kernel on the same stream
+//   (merge_pieces_kernel) merges them.
 //
 // LDS tiles (one direct load writes 64 lanes x 16 bytes contiguously)
 //   K tile: 64 rows x D, row r at r * 2D bytes; its 16-byte granule g is stored
@@ -599,7 +599,7 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
       if (n_ranges > total) n_ranges = total >= 8 ? (int)(total & ~(int64_t)7) : (int)total;
     }
   }
-  // the workspace holds two pieces (and one counter) per workgroup slot
+  // the workspace holds two pieces per workgroup slot
   if (n_ranges > slots) return -2;
   a.n_whole = units - rest;
   a.total = (int64_t)rest * tiles;
@@ -631,7 +631,6 @@ int launch_chunks(AttnArgs& a, hipStream_t stream) {
 
 // Pieces of split units: at most two per range, one range per workgroup
 // slot; sized for the largest configuration of the head dim.
-int attention_ws_counters(int num_cus) { return 3 * num_cus; }
 size_t attention_ws_o_bytes(int num_cus, int head_dim) {
   const int wave_slots = head_dim == 64 ? 12 : 8;  // max waves x workgroups per CU
   return (size_t)2 * num_cus * wave_slots * (head_dim / 32) * 16 * 64 * sizeof(float);

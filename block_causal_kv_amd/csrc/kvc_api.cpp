@@ -57,7 +57,6 @@ struct kvc_cache {
   int num_cus = 0;
   float* ws_o = nullptr;   // attention workspace: partials of split query tiles
   float* ws_ml = nullptr;
-  int* ws_cnt = nullptr;
   int config = 0;  // bf16 attention launch configuration (kv_cache_set_config)
   // Layers.  The root handle owns the pools, the slot table and the layer
   // views; a view (kv_cache_layer) points at its layer's heads in the pools.
@@ -194,18 +193,15 @@ int kv_cache_create_layers(int chunk_tokens, int window_w, int n_sink, int cond_
   if (e == hipSuccess && fp8) e = hipMalloc(&c->amax, sizeof(uint32_t) * 4 * all_heads);
   if (e == hipSuccess && fp8) e = hipMemset(c->amax, 0, sizeof(uint32_t) * 4 * all_heads);
   if (e == hipSuccess && fp8) e = hipMemset(c->scales, 0, sizeof(float) * 2 * all_heads * c->blocks());
-  const int n_cnt = kvc::attention_ws_counters(c->num_cus);
   if (e == hipSuccess) e = hipMalloc(&c->ws_o, kvc::attention_ws_o_bytes(c->num_cus, head_dim));
   if (e == hipSuccess) e = hipMalloc(&c->ws_ml, kvc::attention_ws_ml_bytes(c->num_cus));
-  if (e == hipSuccess) e = hipMalloc(&c->ws_cnt, n_cnt * sizeof(int));
-  if (e == hipSuccess) e = hipMemset(c->ws_cnt, 0, n_cnt * sizeof(int));  // counters start at zero
   // the pool starts as zeros: finite values everywhere, zero padding between slots
   if (e == hipSuccess) e = hipMemset(c->k_pool, 0, c->k_bytes);
   if (e == hipSuccess) e = hipMemset(c->v_pool, 0, c->v_bytes);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
     for (void* p : {(void*)c->k_pool, (void*)c->v_pool, (void*)c->scales, (void*)c->amax, (void*)c->ws_o,
-                    (void*)c->ws_ml, (void*)c->ws_cnt})
+                    (void*)c->ws_ml})
       if (p) (void)hipFree(p);
     (void)hipGetLastError();
     const size_t kb = c->k_bytes, vb = c->v_bytes;
@@ -227,7 +223,7 @@ int kv_cache_destroy(kvc_handle h) {
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) rc = hip_fail(e, "kv_cache_destroy: hipDeviceSynchronize");
   for (void* p : {(void*)h->k_pool, (void*)h->v_pool, (void*)h->scales, (void*)h->amax, (void*)h->ws_o,
-                  (void*)h->ws_ml, (void*)h->ws_cnt})
+                  (void*)h->ws_ml})
     if (p) (void)hipFree(p);
   delete h;
   return rc;
@@ -261,7 +257,6 @@ int kv_cache_layer(kvc_handle h, int layer, kvc_handle* out_view) {
   v->amax = h->amax;
   v->ws_o = h->ws_o;
   v->ws_ml = h->ws_ml;
-  v->ws_cnt = h->ws_cnt;
   try {
     h->views.push_back(v);
   } catch (...) {
@@ -409,7 +404,6 @@ int sink_window_attention_rows(kvc_handle h, int n_q, const void* q, const void*
   a.num_cus = h->num_cus;
   a.ws_o = h->ws_o;
   a.ws_ml = h->ws_ml;
-  a.ws_cnt = h->ws_cnt;
   if (h->kv_dtype == KVC_KV_FP8) {
     // every chunk has its own scales: one segment per block, the current chunk
     // quantised into the spare slot after the window slots

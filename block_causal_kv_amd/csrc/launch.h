@@ -28,11 +28,11 @@ struct AttnArgs {
   int q_rows;    // query rows per tile (the last tile of a head may hold fewer)
   // work split (set by the launcher): n_whole units are computed whole, by
   // grid_whole blocks (a multiple of 8).  fp8 kernel: the remaining `rest`
-  // units are each cut into `slices` key-tile ranges whose partial results are
-  // merged by the slice that finishes last.  bf16 kernel: the (unit, key tile)
-  // space of the remaining units (`total` tiles) is cut into n_ranges equal
-  // contiguous ranges, one per workgroup; a unit that straddles ranges is
-  // computed in pieces merged by the piece finishing last.
+  // units are each cut into `slices` key-tile ranges.  bf16 kernel: the
+  // (unit, key tile) space of the remaining units (`total` tiles) is cut into
+  // n_ranges equal contiguous ranges, one per workgroup; a unit that
+  // straddles ranges is computed in pieces.  Pieces and slices leave partial
+  // results that a merge kernel, launched next on the same stream, combines.
   int tiles;     // key tiles of one unit (all segments + the current chunk)
   int n_whole;
   int rest;
@@ -42,7 +42,6 @@ struct AttnArgs {
   int64_t total;
   float* ws_o;     // partial O^T of the slices: [piece][wave][register][lane]
   float* ws_ml;    // partial (max, sum): [piece][wave][2][lane]
-  int* ws_cnt;     // finished pieces per split unit; zero between calls
   int num_cus;
   // whole-stream form (kernel's stream mode): chunks 0..n_chunks-1 of one input
   int n_chunks;
@@ -68,11 +67,10 @@ struct AttnArgs {
 };
 
 // bf16 attention: one workgroup per (head, query tile of up to 32 rows per wave).
-// Workspace of the split units: bytes of ws_o and ws_ml, and counters, for a
-// device with num_cus compute units.
+// Workspace of the split units: bytes of ws_o and ws_ml for a device with
+// num_cus compute units.
 size_t attention_ws_o_bytes(int num_cus, int head_dim);
 size_t attention_ws_ml_bytes(int num_cus);
-int attention_ws_counters(int num_cus);
 // config: index into the launch configurations of the head dim (0 = default);
 // attention_bf16_configs lists them (waves per workgroup, workgroups per CU)
 // and returns their number.

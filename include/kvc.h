@@ -203,7 +203,10 @@ int kv_cache_query(kvc_handle h, int64_t* next_chunk_id, int* occupancy, int64_t
  * keys j of the condition tokens, every chunk resident in the cache, and the
  * chunk's own T tokens.  The call first writes v_cur (bf16: transposed; fp8:
  * k_cur too, quantised like an append with per-head scales) into the pool's
- * spare slot, so two calls on one cache must not run concurrently.
+ * spare slot, and split query tiles leave partial results in the cache's
+ * workspace for a merge kernel launched after the attention kernel; so two
+ * calls on one cache (or on layer views of one cache) must not run
+ * concurrently on different streams.
  * Errors: INVALID, HIP.
  */
 int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const void* v_cur,
