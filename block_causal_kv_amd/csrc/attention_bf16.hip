@@ -262,10 +262,13 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
       if constexpr (STREAM) return s < has_cond ? a.cond_len : T;
       return s < a.nseg ? a.seg_len[s] : T;
     };
+    // the next key tile; a cache call's unit is walked cyclically, so after
+    // the current chunk (segment nseg) comes segment 0
     auto advance = [&](Cursor cur) -> Cursor {
       cur.off += C::BN;
       if (cur.off >= cur.len) {
         cur.seg += 1;
+        if (!STREAM && cur.seg > a.nseg) cur.seg = 0;
         cur.off = 0;
         cur.len = seg_len(cur.seg);
       }
@@ -405,15 +408,22 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
       l_run += rs;
     };
 
-    // ---- main loop over key tiles [t0, t1), unrolled by two so each half reads
-    // a fixed buffer.  At the top of a step the tile in buffer `buf` is complete
-    // in LDS (barrier) and the other buffer's previous tile has been read by
-    // every wave (same barrier), so the next tile's loads go there while this
-    // tile is computed.
+    // A unit of the split round takes its key tiles cyclically from tile rot
+    // on, where rot is how far into its range the unit begins: a range then
+    // reads key tile j*L + tau (mod tiles) at step tau, for a small j and the
+    // range length L, so the query tiles of a head that run side by side on
+    // one XCD read a few common windows of its K/V rather than as many
+    // offsets as there are ranges, and the fetches are shared through L2.
+    // (The order of a unit's key tiles changes its result only by rounding.)
+    int rot = 0;
+    if (!STREAM && unit >= a.n_whole) {
+      const int64_t u0 = (int64_t)(unit - a.n_whole) * a.tiles;  // in the split round's space
+      rot = (int)((u0 - range_lo(range_of(u0, a.total, a.n_ranges), a.total, a.n_ranges)) % a.tiles);
+    }
     Cursor cur;
     {
-      int rem = t0, sg = 0;
-      for (;;) {  // segment holding tile t0 (t0 < tiles, so this ends)
+      int rem = STREAM ? t0 : (t0 + rot) % a.tiles, sg = 0;
+      for (;;) {  // segment holding that tile (it is < tiles, so this ends)
         const int len = seg_len(sg);
         const int nt = (len + C::BN - 1) / C::BN;
         if (rem < nt) {
@@ -424,6 +434,11 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
         ++sg;
       }
     }
+    // ---- main loop over key tiles [t0, t1), unrolled by two so each half reads
+    // a fixed buffer.  At the top of a step the tile in buffer `buf` is complete
+    // in LDS (barrier) and the other buffer's previous tile has been read by
+    // every wave (same barrier), so the next tile's loads go there while this
+    // tile is computed.
     int left = uniform(t1 - t0);  // >= 1
     {
       const Plan p0 = make_plan(cur, 0);
@@ -576,20 +591,21 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
   //  aligned:   n_ranges = rest * s, s = slots / rest: every range is exactly
   //             1/s of a unit, so the query tiles of a head still stream the
   //             same K/V in step (slice k of each);
-  //  unaligned: n_ranges = slots: equal work per slot, but ranges start at
-  //             arbitrary key offsets and every workgroup fetches its own K/V
-  //             stream past L2 (measured about 1.25x slower per tile at
-  //             720p-sized K/V).
+  //  unaligned: n_ranges = slots: equal work per slot; each unit is walked
+  //             cyclically from where its range meets it (see the kernel), so
+  //             the ranges of a head still share a few K/V windows in L2.
+  //             Measured: about the ideal rest/slots of a round plus a fixed
+  //             0.08 round (pieces per range, partial writes, the merge).
   // A last round that is nearly full is run whole instead.  Costs are in units
-  // of one whole-unit round; a split pays a small merge cost per slice (the
-  // merge kernel reads one more partial per slice).
+  // of one whole-unit round; an aligned split pays a small merge cost per
+  // slice (the merge kernel reads one more partial per slice).
   const int slots = WGS * a.num_cus;
   int rest = a.ws_o == nullptr ? 0 : units % slots;
   int n_ranges = 0;
   if (rest > 0) {
     const int s = slots / rest;
     const double aligned = 1.0 / s + (s > 1 ? 0.005 * s : 0.0);
-    const double unaligned = 1.25 * rest / slots + 0.01;
+    const double unaligned = (double)rest / slots + 0.08;
     const double whole = units > slots ? 1.0 : 1e30;  // (only when other rounds exist)
     if (whole <= aligned && whole <= unaligned) {
       rest = 0;
