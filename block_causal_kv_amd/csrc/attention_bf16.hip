@@ -248,6 +248,13 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
     const u32x4 rv_pool = make_rsrc(a.vt + (int64_t)head * D * a.rows_v, (uint32_t)(D * a.rows_v * 2));
     const u32x4 rv_ws = STREAM ? make_rsrc(a.vt_ws + (int64_t)head * D * a.ws_rows, (uint32_t)(D * a.ws_rows * 2))
                                : rv_pool;
+    // byte offsets of this lane's V^T granules from a tile's first column
+    uint32_t vo_pool[C::LPW], vo_ws[C::LPW];
+#pragma unroll
+    for (int j = 0; j < C::LPW; ++j) {
+      vo_pool[j] = vdr[j] * (uint32_t)(a.rows_v * 2) + 2 * vkey[j];
+      vo_ws[j] = STREAM ? vdr[j] * (uint32_t)(a.ws_rows * 2) + 2 * vkey[j] : 0u;
+    }
 
     f32x16 oacc[C::DB];
 #pragma unroll
@@ -262,6 +269,13 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
       if constexpr (STREAM) return s < has_cond ? a.cond_len : T;
       return s < a.nseg ? a.seg_len[s] : T;
     };
+    // cache call: pool row of segment s's first key; for the current chunk
+    // (segment nseg) the column of its V^T in the spare slot
+    auto seg_row = [&](int s) -> int {
+      if constexpr (STREAM) return 0;
+      s = uniform(s);
+      return s < a.nseg ? a.seg_row0[s] : a.cur_row0;
+    };
     // the next key tile; a cache call's unit is walked cyclically, so after
     // the current chunk (segment nseg) comes segment 0
     auto advance = [&](Cursor cur) -> Cursor {
@@ -271,6 +285,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
         if (!STREAM && cur.seg > a.nseg) cur.seg = 0;
         cur.off = 0;
         cur.len = seg_len(cur.seg);
+        cur.row0 = seg_row(cur.seg);
       }
       return cur;
     };
@@ -299,10 +314,9 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
       } else {
         k_pool = s < a.nseg;
         v_pool = true;
-        row0 = (k_pool ? a.seg_row0[s] : 0) + cur.off;
-        vcol0 = (k_pool ? a.seg_row0[s] : a.cur_row0) + cur.off;
+        row0 = (k_pool ? cur.row0 : 0) + cur.off;
+        vcol0 = cur.row0 + cur.off;
       }
-      const uint32_t vstride = (uint32_t)uniform((int)(v_pool ? a.rows_v : a.ws_rows) * 2);
       p.kso = (uint32_t)uniform(row0 * C::RB);
       p.vso = (uint32_t)uniform(vcol0 * 2);
       p.rk = make_rsrc(k_pool ? kpool_h : kcur_h, k_pool ? kpool_bytes : kcur_bytes);
@@ -312,7 +326,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
       // V^T granules wholly past the segment read as zero, so no stale value of a
       // neighbouring slot meets a zero probability (0 * inf would be NaN).
 #pragma unroll
-      for (int j = 0; j < C::LPW; ++j) p.vo[j] = vkey[j] < valid ? vdr[j] * vstride + 2 * vkey[j] : kOutOfRange;
+      for (int j = 0; j < C::LPW; ++j) p.vo[j] = vkey[j] < valid ? (v_pool ? vo_pool[j] : vo_ws[j]) : kOutOfRange;
       return p;
     };
     auto load_one = [&](const Plan& p, int i) {  // i < LPW: K block i, else V^T block i - LPW
@@ -427,7 +441,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
         const int len = seg_len(sg);
         const int nt = (len + C::BN - 1) / C::BN;
         if (rem < nt) {
-          cur = {sg, rem * C::BN, len};
+          cur = {sg, rem * C::BN, len, seg_row(sg)};
           break;
         }
         rem -= nt;

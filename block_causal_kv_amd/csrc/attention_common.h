@@ -45,11 +45,14 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
 
 
 // Segment cursor over [pool segments..., current chunk]; wave-uniform.  The
-// segment length is cached so the table is read only when a segment starts.
+// segment's length and first pool row are cached so the segment table (in
+// kernel-argument memory) is read only when a segment starts: a scalar load
+// per tile would put a memory round trip at the head of every tile.
 struct Cursor {
   int seg;
   int off;
   int len;
+  int row0 = 0;
 };
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }

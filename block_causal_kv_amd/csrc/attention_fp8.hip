@@ -244,6 +244,7 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
       cur.seg += 1;
       cur.off = 0;
       cur.len = cur.seg < a.nseg ? seg_len(cur.seg) : 0;
+      cur.row0 = cur.seg < a.nseg ? a.seg_row0[uniform(cur.seg)] : 0;
     }
     return cur;
   };
@@ -253,8 +254,7 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
   };
   auto make_plan = [&](Cursor cur, int buf) -> Plan {
     Plan p;
-    const int s = uniform(cur.seg);
-    const int row0 = a.seg_row0[s] + cur.off;  // pool row of the tile's first key
+    const int row0 = cur.row0 + cur.off;  // pool row of the tile's first key
     p.kso = (uint32_t)uniform(row0 * D);
     p.vso = (uint32_t)uniform(row0);
     p.dst = (uint32_t)uniform((int)(lds0 + buf * C::BUF_B));
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
       const int len = seg_len(sg);
       const int nt = (len + BN - 1) / BN;
       if (rem < nt) {
-        cur = {sg, rem * BN, len};
+        cur = {sg, rem * BN, len, a.seg_row0[sg]};
         break;
       }
       rem -= nt;
