@@ -93,7 +93,8 @@ struct Cfg {
   static constexpr int TILE_B = BN * RB;     // bytes of a K tile (= bytes of a V^T tile)
   static constexpr int VRB = BN * 2;         // bytes of a V^T tile row
   static constexpr int LPW = TILE_B / 1024 / NW;  // 1 KB direct loads per wave, per tensor
-  static constexpr int BUF_B = 2 * TILE_B;   // one LDS buffer: K tile then V^T tile
+  static constexpr bool PP = NW == 8;        // ping-pong schedule (two wave groups per SIMD pair)
+  static constexpr int NBUF = PP ? 4 : 2;    // tile buffers: K tiles first, then the V^T tiles
   static constexpr int DS = D / 16;          // MFMA k-steps over the head dim
   static constexpr int DB = D / 32;          // 32-wide output blocks over the head dim
   static constexpr int KB = BN / 32;         // 32-key blocks per tile
@@ -113,7 +114,7 @@ __device__ inline int range_of(int64_t g, int64_t total, int n) { return (int)((
 template <int D, int NW, int WGS, bool STREAM>
 __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a) {
   using C = Cfg<D, NW>;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::BUF_B];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::NBUF * C::TILE_B];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
   const uint32_t kblk = (uint32_t)uniform((int)(lds0 + wave * C::LPW * 1024));  // this wave's K blocks, buffer 0
-  const uint32_t vblk = kblk + C::TILE_B;
+  const uint32_t vblk = kblk + C::NBUF * C::TILE_B;
 
   // ---- per-lane LDS read offsets of the MFMA operands (buffer 0; + kb/db blocks as immediates)
   const int krow = 16 * (col >> 4) + 8 * ((col >> 2) & 1) + 4 * ((col >> 3) & 1) + (col & 3);
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
     kaddr[ds] = (uint32_t)(krow * C::RB + ((2 * ds + hf) ^ swz_k<D>(krow)) * 16);
 #pragma unroll
   for (int ks = 0; ks < C::BN / 16; ++ks)
-    vaddr[ks] = (uint32_t)(C::TILE_B + col * C::VRB + ((2 * ks + hf) ^ swz_v(col)) * 16);
+    vaddr[ks] = (uint32_t)(C::NBUF * C::TILE_B + col * C::VRB + ((2 * ks + hf) ^ swz_v(col)) * 16);
 
   // ---- the work items of this workgroup: the pieces of the units its range
   // covers (cache call), or its one unit (stream form)
@@ -287,6 +288,12 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
         cur.len = seg_len(cur.seg);
         cur.row0 = seg_row(cur.seg);
       }
+      // (wave-uniform by construction; said explicitly so the compiler keeps
+      // the cursor in scalar registers)
+      cur.seg = uniform(cur.seg);
+      cur.off = uniform(cur.off);
+      cur.len = uniform(cur.len);
+      cur.row0 = uniform(cur.row0);
       return cur;
     };
 
@@ -321,8 +328,8 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
       p.vso = (uint32_t)uniform(vcol0 * 2);
       p.rk = make_rsrc(k_pool ? kpool_h : kcur_h, k_pool ? kpool_bytes : kcur_bytes);
       p.rv = v_pool ? rv_pool : rv_ws;
-      p.kdst = (uint32_t)uniform((int)(kblk + buf * C::BUF_B));
-      p.vdst = (uint32_t)uniform((int)(vblk + buf * C::BUF_B));
+      p.kdst = (uint32_t)uniform((int)(kblk + buf * C::TILE_B));
+      p.vdst = (uint32_t)uniform((int)(vblk + buf * C::TILE_B));
       // V^T granules wholly past the segment read as zero, so no stale value of a
       // neighbouring slot meets a zero probability (0 * inf would be NaN).
 #pragma unroll
@@ -336,6 +343,19 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
         load_lds16(p.rv, p.vdst + (i - C::LPW) * 1024, p.vo[i - C::LPW], p.vso);
     };
 
+    // mask the scores of keys >= valid (a partial last tile of a segment).  The
+    // key of register k of 32-key block kb is kb*32 + 16*(k/8) + 8*hf + k%8;
+    // comparing one per-lane value with constants keeps the compiler from
+    // holding 32 precomputed key indices in registers for this rare path.
+    auto mask_tail = [&](f32x16 (&s)[C::KB], int valid) {
+      const int lim = valid - 8 * hf;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if (kb * 32 + 16 * (k >> 3) + (k & 7) >= lim) s[kb][k] = kNegInf;
+    };
+
     // ---- one key tile from LDS buffer BUF
     auto compute = [&](auto buf_tag, int valid, const Plan& nplan, bool more) {
       constexpr int BUF = decltype(buf_tag)::value;
@@ -345,7 +365,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
           for (int i = 0; i < 2 * C::LPW; ++i) load_one(nplan, i);
         return;
       }
-      const uint8_t* kl = lds + BUF * C::BUF_B;
+      const uint8_t* kl = lds + BUF * C::TILE_B;
       // ---- S^T = K . Q^T
       f32x16 sacc[C::KB];
 #pragma unroll
@@ -362,14 +382,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
           if (kb == C::KB - 1 && more && ds % (C::DS / (2 * C::LPW)) == 0)
             load_one(nplan, ds / (C::DS / (2 * C::LPW)));
         }
-      // ---- mask the tail of a partial tile: key of register k = kb*32 + 16*(k/8) + 8*hf + k%8
-      if (valid < C::BN) {
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-          for (int k = 0; k < 16; ++k)
-            if (kb * 32 + 16 * (k >> 3) + 8 * hf + (k & 7) >= valid) sacc[kb][k] = kNegInf;
-      }
+      if (valid < C::BN) mask_tail(sacc, valid);
       // ---- online softmax
       bf16x8 pb[C::KB][2];  // P^T operands: [32-key block][16-key half]
       float mx = kNegInf;
@@ -448,6 +461,177 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
         ++sg;
       }
     }
+    if constexpr (C::PP) {
+      // ---- ping-pong schedule.  SIMD s holds wave s (group A) and wave s + 4
+      // (group B).  Per key tile j every wave runs two phases:
+      //   X_j: S(j) = K(j) Q^T and O^T += V(j-1)^T P(j-1)^T (32 MFMAs), then
+      //        the row max of S(j)
+      //   Y_j: the loads of tile j + 2, the softmax of S(j) -> P(j)
+      // Group B runs one phase behind group A and a workgroup barrier ends
+      // every phase, so on each SIMD one wave streams MFMAs while the other
+      // runs the exponentials.  (An MFMA holds up its own wave's issue for
+      // most of its duration, so VALU work overlaps MFMAs only when it comes
+      // from the other wave.)
+      // Global phase p: group A runs X_{p/2} (p even) or Y_{(p-1)/2}, group B
+      // one phase later.  Tile j lives in LDS buffer j % 4: loaded during
+      // phases 2j-3 (A's Y_{j-2}) and 2j-2 (B's Y_{j-2}), after the last reads
+      // of tile j-4 (phase 2j-5); its K is read in phases 2j, 2j+1, its V^T in
+      // 2j+2, 2j+3.  Each wave waits for its own loads of tile j by the end of
+      // phase 2j-1, the barrier that opens tile j.
+      const int grp = wave >> 2;
+      const int n = uniform(t1 - t0);  // key tiles of this item, >= 1
+      Cursor lcur = cur;               // the tile whose loads were issued last
+      {
+        const Plan p = make_plan(lcur, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * C::LPW; ++i) load_one(p, i);
+      }
+      if (n > 1) {
+        lcur = advance(lcur);
+        const Plan p = make_plan(lcur, 1);
+#pragma unroll
+        for (int i = 0; i < 2 * C::LPW; ++i) load_one(p, i);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      if (grp == 1) __syncthreads();  // group B starts one phase late
+      Cursor ccur = cur;              // tile j, for the mask of a partial tile
+      f32x16 sacc[C::KB];
+      bf16x8 pb[C::KB][2];
+      float mx = 0.f;                 // row max of S(j), scaled (X_j -> Y_j)
+      // X: S(j) = K(j) Q^T from buffer j % 4 (DO_S), then O^T += V(j-1)^T
+      // P(j-1)^T from buffer (j-1) % 4 (DO_PV), then the row max of S(j).
+      // The buffer offsets are wave-uniform multiples of the tile size, OR-ed
+      // into the lane addresses.  Operand reads run RA ahead of their MFMAs
+      // through a ring of registers; sched_barrier keeps that order (the
+      // scheduler would otherwise chain MFMAs of one accumulator back to back
+      // and wait on single reads).  The row max sits here rather than in Y:
+      // this wave waits at the barrier anyway while the other one runs the
+      // exponentials, which are the longer half.
+      auto phase_x = [&](auto do_s, auto do_pv, int j) {
+        constexpr bool DO_S = decltype(do_s)::value, DO_PV = decltype(do_pv)::value;
+        constexpr int NS = DO_S ? C::KB * C::DS : 0;              // S: k-step outer, key block inner
+        constexpr int NM = NS + (DO_PV ? 2 * C::KB * C::DB : 0);  // PV: (kb, h2) outer, dim block inner
+        constexpr int RA = 6;
+        if (!wave_active) return;
+        const uint32_t kofs = (uint32_t)uniform((j & 3) * C::TILE_B);
+        const uint32_t vofs = (uint32_t)uniform(((j + 3) & 3) * C::TILE_B);
+        auto rd = [&](int i) -> uint4 {  // the LDS operand of MFMA i
+          if (i < NS) return *(const uint4*)(lds + (kofs | kaddr[i / C::KB]) + (i % C::KB) * 32 * C::RB);
+          const int q = i - NS;
+          return *(const uint4*)(lds + (vofs | vaddr[q / C::DB]) + (q % C::DB) * 32 * C::VRB);
+        };
+        auto mm = [&](int i, uint4 raw) {
+          const bf16x8 a_op = __builtin_bit_cast(bf16x8, raw);
+          if (i < NS) {
+            const int kb = i % C::KB;
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_op, qreg[i / C::KB], sacc[kb], 0, 0, 0);
+          } else {
+            const int q = i - NS, db = q % C::DB, kh = q / C::DB;
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_op, pb[kh >> 1][kh & 1], oacc[db], 0, 0, 0);
+          }
+        };
+        if constexpr (DO_S) {
+#pragma unroll
+          for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int k = 0; k < 16; ++k) sacc[kb][k] = 0.f;
+        }
+        uint4 ring[RA];
+#pragma unroll
+        for (int i = 0; i < RA; ++i)
+          if (i < NM) ring[i] = rd(i);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          mm(i, ring[i % RA]);
+          if (i + RA < NM) ring[i % RA] = rd(i + RA);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (DO_S) {
+          const int valid = uniform(min(C::BN, ccur.len - ccur.off));
+          if (valid < C::BN) mask_tail(sacc, valid);
+          float mx0 = kNegInf, mx1 = kNegInf;  // two independent chains
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            mx0 = fmaxf(mx0, sacc[0][k]);
+            mx1 = fmaxf(mx1, sacc[C::KB - 1][k]);
+          }
+          mx = max_halves(fmaxf(mx0, mx1)) * c;
+        }
+      };
+      // Y: the loads of tile j + 2 and the softmax of S(j) -> P(j).
+      // Returns whether loads were issued.
+      auto phase_y = [&](int j) -> bool {
+        bool issued = false;
+        if (j + 2 < n) {
+          lcur = advance(lcur);
+          const Plan p = make_plan(lcur, (j + 2) & 3);
+#pragma unroll
+          for (int i = 0; i < 2 * C::LPW; ++i) load_one(p, i);
+          issued = true;
+        }
+        if (wave_active) {
+          if (__any(mx > m_run + kRescaleSlack)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+              for (int k = 0; k < 16; ++k) oacc[db][k] *= alpha;
+          }
+          // P = exp2(s*c - m) as bf16; the row sum adds the same bf16 values
+          // that enter the PV product (two independent chains)
+          float rs[2] = {0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              unsigned w[4];
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][h2 * 8 + 2 * k], c, -m_run));
+                const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][h2 * 8 + 2 * k + 1], c, -m_run));
+                w[k] = pack_bf16(p0, p1);
+                rs[h2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[k]),
+                                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), rs[h2], false);
+              }
+              const u32x4 wv = {w[0], w[1], w[2], w[3]};
+              pb[kb][h2] = __builtin_bit_cast(bf16x8, wv);
+            }
+          l_run += rs[0] + rs[1];
+        }
+        ccur = advance(ccur);
+        return issued;
+      };
+      // barriers: group A waits for its own loads at the end of its Y phases,
+      // group B at the end of its X phases (both odd global phases)
+      auto end_x = [&]() {
+        if (grp == 1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+      };
+      auto end_y = [&](bool issued) {
+        if (grp == 0) {
+          if (issued)
+            __builtin_amdgcn_s_waitcnt((0x0F70 & ~0xF) | (2 * C::LPW));  // all but this phase's loads
+          else
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+        }
+        __syncthreads();
+      };
+      phase_x(std::true_type(), std::false_type(), 0);
+      end_x();
+      for (int j = 1; j < n; ++j) {
+        end_y(phase_y(j - 1));
+        phase_x(std::true_type(), std::true_type(), j);
+        end_x();
+      }
+      end_y(phase_y(n - 1));
+      phase_x(std::false_type(), std::true_type(), n);
+      end_x();
+      if (grp == 0) __syncthreads();  // group A's trailing phase
+    } else {
     // ---- main loop over key tiles [t0, t1), unrolled by two so each half reads
     // a fixed buffer.  At the top of a step the tile in buffer `buf` is complete
     // in LDS (barrier) and the other buffer's previous tile has been read by
@@ -477,6 +661,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
       cur = nxt;
+    }
     }
 
     // ---- a piece of a unit split between ranges: leave the partial result
