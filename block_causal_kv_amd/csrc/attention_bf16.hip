@@ -502,7 +502,9 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
       // X: S(j) = K(j) Q^T from buffer j % 4 (DO_S), then O^T += V(j-1)^T
       // P(j-1)^T from buffer (j-1) % 4 (DO_PV), then the row max of S(j).
       // The buffer offsets are wave-uniform multiples of the tile size, OR-ed
-      // into the lane addresses.  Operand reads run RA ahead of their MFMAs
+      // into the lane addresses (a lane's K address lies below one tile; its
+      // V^T address is the V^T region's base, a multiple of four tiles, plus
+      // less than one tile: the OR is an add).  Operand reads run RA ahead of their MFMAs
       // through a ring of registers; sched_barrier keeps that order (the
       // scheduler would otherwise chain MFMAs of one accumulator back to back
       // and wait on single reads).  The row max sits here rather than in Y:
