@@ -12,13 +12,22 @@
 //                                     E4M3 parts (q / sq = hi + lo / 16, sq =
 //                                     row amax / 448); the lo product takes an
 //                                     exact 2^-4 through the MFMA's block scale.
-//   O^T += Vc^T . P8^T                P8 = E4M3 of the probabilities times
-//                                     vs_tile / vs_ref (<= 1), so tiles of
-//                                     chunks with different V scales share one
-//                                     accumulator.
+//   O^T += Vc^T . P8^T                P8 = E4M3 of 2^kP8Offset times the
+//                                     probabilities times vs_tile / vs_ref
+//                                     (<= 1), so tiles of chunks with
+//                                     different V scales share one accumulator.
 // The true score is sq * sk * (S^T row), so the K scale and the row's Q scale
-// fold into the softmax FMA constant; the V scale folds into the exponent; the
-// softmax denominator sums the unquantised probabilities.
+// fold into the softmax FMA constant; the V scale folds into the exponent.
+//
+// Range of P8: E4M3 resolves nothing below 2^-9, so probabilities are taken
+// relative to 2^-kP8Offset of the running maximum, and the maximum may run
+// ahead of the last rescale by at most kP8Slack (2^(6 + 2.75) = 430 < 448, the
+// largest E4M3 value).  Probabilities down to 2^-15 of the row maximum then
+// survive; with the maximum mapped to 1 a row whose mass lies in many keys
+// far below its maximum would lose most of it.  The denominator sums the same
+// E4M3 values the numerator uses (an MFMA against an all-ones operand), so
+// each output row is a convex combination of V rows: adding a constant to V
+// adds it to the output.
 //
 // Layout: every segment (condition rows, each resident slot, and the current
 // chunk quantised into the spare slot) is its own segment because scales are
@@ -45,6 +54,9 @@ namespace kvc {
 namespace {
 
 using namespace dev;
+
+constexpr float kP8Offset = 6.0f;  // log2 of the scale of P8 over the running maximum
+constexpr float kP8Slack = 2.75f;  // lazy-rescale slack of the fp8 kernel (log2 units)
 
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 
@@ -196,6 +208,24 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
   const float cq = a.c * sq;  // per-lane part of the score scale
+  // Row sums of P8 by MFMA against an all-ones operand (E4M3 1.0 = 0x38): every
+  // row of lacc holds the sum over the tile's 64 keys of the very E4M3 values
+  // the numerator uses.  P8 carries the segment's V-scale ratio, so lacc
+  // collects one segment at a time and is folded into l_run, without that
+  // ratio, when the walk leaves the segment (lseg).  l_run keeps the per-half
+  // convention of the kernel (the halves are summed at the end): each half adds
+  // half of the full sum.
+  f32x16 lacc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
+  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                      0x38383838, 0x38383838, 0x38383838, 0x38383838};
+  int lseg = -1;
+  auto flush_sum = [&]() {
+    if (lseg >= 0) l_run += 0.5f * lacc[0] * __builtin_amdgcn_exp2f(-s_lv[lseg]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
+  };
 
   // ---- buffer resources of this head's code rows (range-checked)
   const int64_t prows = a.pool_rows8;
@@ -281,6 +311,10 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
     }
     const int valid = min(BN, cur.len - cur.off);
     const int sg = uniform(cur.seg);
+    if (sg != lseg) {
+      flush_sum();
+      lseg = sg;
+    }
     const float mult = cq * s_ks[sg];  // score = raw * mult (log2 domain)
     const float lvsr = s_lv[sg];       // <= 0
     const uint8_t* tl = lds + BUF * C::BUF_B;
@@ -316,7 +350,7 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     mx = max_halves(mx) * mult;
-    if (__any(mx > m_run + kRescaleSlack)) {
+    if (__any(mx > m_run + kP8Slack)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -325,9 +359,10 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
     }
-    const float bias = lvsr - m_run;
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+    const float bias = lvsr - m_run + kP8Offset;
     unsigned pw[8];  // 32 E4M3 probabilities of this lane half, register (= key) order
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -337,11 +372,8 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
         const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 1], mult, bias));
         const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 2], mult, bias));
         const float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 3], mult, bias));
-        rs[w] += (e0 + e1) + (e2 + e3);
         pw[kb * 4 + w] = pk_fp8(e0, e1) | (pk_fp8(e2, e3) << 16);
       }
-    // the sums carry the factor vs_tile / vs_ref; the denominator must not
-    l_run += ((rs[0] + rs[1]) + (rs[2] + rs[3])) * __builtin_amdgcn_exp2f(-lvsr);
     const i32x8 pv = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
     // ---- O^T += Vc^T . P8^T (one 64-key MFMA per 32 dims)
 #pragma unroll
@@ -351,6 +383,7 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
       const i32x8 va = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pv, oacc[db], 0, 0, 0, 127, 0, 127);
     }
+    lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pv, lacc, 0, 0, 0, 127, 0, 127);
   };
 
   // ---- main loop over key tiles [t0, t1), unrolled by two (fixed LDS buffers)
@@ -394,6 +427,8 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
     cur = nxt;
   }
 
+  flush_sum();
+
   // ---- a slice of a split unit: leave the partial result, scaled by vs_ref
   // (every slice of a unit uses the same vs_ref), for merge_slices_kernel
   if (piece >= 0) {
@@ -422,7 +457,8 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
         const uint32_t w1 = (uint32_t)f2bf(oacc[db][4 * g + 2] * f) | ((uint32_t)f2bf(oacc[db][4 * g + 3] * f) << 16);
         *(uint2*)(dst + db * 32 + 8 * g) = make_uint2(w0, w1);
       }
-    if (a.lse != nullptr && hf == 0) a.lse[head_rows + qrow] = (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+    if (a.lse != nullptr && hf == 0)
+      a.lse[head_rows + qrow] = (m_run - kP8Offset + __log2f(l_tot)) * 0.69314718055994530942f;
   }
 }
 
@@ -472,7 +508,7 @@ __global__ __launch_bounds__(64) void merge_slices_kernel(AttnArgs a) {
       *(uint2*)(dst + db * 32 + 8 * g) = make_uint2(w0, w1);
     }
   if (a.lse != nullptr && hf == 0)
-    a.lse[(int64_t)head * a.Tq + qrow] = (m + __log2f(l_tot)) * 0.69314718055994530942f;
+    a.lse[(int64_t)head * a.Tq + qrow] = (m - kP8Offset + __log2f(l_tot)) * 0.69314718055994530942f;
 }
 
 constexpr int kMaxSlicesF8 = 8;
