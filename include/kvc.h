@@ -206,7 +206,11 @@ int kv_cache_query(kvc_handle h, int64_t* next_chunk_id, int* occupancy, int64_t
  * spare slot, and split query tiles leave partial results in the cache's
  * workspace for a merge kernel launched after the attention kernel; so two
  * calls on one cache (or on layer views of one cache) must not run
- * concurrently on different streams.
+ * concurrently on different streams.  fp8 caches compute both products on
+ * fp8 MFMA: Q is split per row into two E4M3 parts, the probabilities are held
+ * as E4M3 values scaled to the top of that format's range, and each row is
+ * normalised by the sum of those same values, so an output row is a convex
+ * combination of the stored (dequantised) V rows.
  * Errors: INVALID, HIP.
  */
 int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const void* v_cur,
