@@ -43,8 +43,11 @@ def errors(o: np.ndarray, ref: np.ndarray):
 
 def dequant(x: np.ndarray) -> np.ndarray:
     """What an fp8 cache stores for a [H][N][D] tensor: E4M3 codes times one
-    float32 scale per head (oracle's quantiser)."""
+    float32 scale per head (oracle's quantiser).  An empty tensor (no condition
+    tokens) stores nothing."""
     from oracle import fp8 as ofp8
+    if x.size == 0:
+        return x
     codes, scales = ofp8.quantize_heads(x)
     return ofp8.dequantize_heads(codes, scales)
 
