@@ -167,3 +167,31 @@ def test_rejected_arguments():
         f8.attention_chunks(x, x, x)
     assert e.value.code == _lib.KVC_ERR_UNSUPPORTED
     f8.close()
+
+
+def _sweep_cases(n=16, seed=4048):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        D = int(rng.choice([64, 128]))
+        out.append(dict(name="csweep%d" % i, n_chunks=int(rng.integers(1, 9)),
+                        chunk_tokens=int(np.exp(rng.uniform(0.0, np.log(400.0)))), cond_len=int(rng.integers(0, 200)),
+                        heads=int(rng.integers(1, 7)), head_dim=D, window=int(rng.integers(1, 6)),
+                        n_sink=int(rng.integers(0, 3)), seed=300 + i, outlier_frac=0.01,
+                        config=int(rng.integers(0, 3 if D == 64 else 2))))
+    return out
+
+
+SWEEP = _sweep_cases()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("kw", SWEEP, ids=[c["name"] for c in SWEEP])
+def test_shape_sweep_one_call(kw):
+    """Seeded sweep of small shapes (T log-uniform over 1 .. 399, Lc, H, D, W,
+    sinks, chunk count and launch configuration drawn): every chunk, every
+    row, against the oracle's per-chunk form."""
+    kw = dict(kw)
+    config = kw.pop("config")
+    spec = synthetic.small_spec(**kw)
+    run_chunks(spec, spec.n_chunks, full_mask=False, config=config)
