@@ -10,7 +10,7 @@ import pytest
 import synthetic
 from oracle.cache import CacheModel
 from oracle.stream import attend_chunk, attend_queries
-from streams import BF16_MAX_ABS, BF16_REL_L2, FP8_REL_L2, LSE_TOL, dequant, errors, from_dev, say, to_dev
+from streams import BF16_MAX_ABS, BF16_REL_L2, FP8_LSE_TOL, FP8_REL_L2, LSE_TOL, dequant, errors, from_dev, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -22,6 +22,7 @@ def _check(og, lg, ref, ref_lse, fp8, what):
     assert np.isfinite(og).all(), what
     if fp8:
         assert rl <= FP8_REL_L2, (what, rl)
+        assert le <= FP8_LSE_TOL, (what, le)
     else:
         assert ma <= BF16_MAX_ABS and rl <= BF16_REL_L2, (what, ma, rl)
         assert le <= LSE_TOL, (what, le)
@@ -110,3 +111,38 @@ def test_condition_rows_rejected():
         c.set_condition(torch.zeros((2, 40, 128), dtype=torch.bfloat16, device="cuda"),
                         torch.zeros((2, 40, 128), dtype=torch.bfloat16, device="cuda"))
     c.close()
+
+
+def _sweep_cases(n=12, seed=5151):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        fp8 = i % 4 == 3
+        D = int(rng.choice([64, 128]))
+        T = int(np.exp(rng.uniform(0.0, np.log(400.0))))
+        Lc = int(rng.integers(0, 160))
+        new_rows = int(rng.integers(0, Lc + 1))
+        if fp8:
+            T, Lc, new_rows = max(16, T // 16 * 16), Lc // 16 * 16, new_rows // 16 * 16
+            new_rows = min(new_rows, Lc)
+        W = int(rng.integers(1, 4))
+        n_sink = int(rng.integers(0, 3))
+        out.append(dict(spec=dict(name="qsweep%d" % i, n_chunks=n_sink + W + 2, chunk_tokens=T, cond_len=Lc,
+                                  heads=int(rng.integers(1, 5)), head_dim=D, window=W, n_sink=n_sink,
+                                  seed=400 + i, outlier_frac=0.01, kv_dtype="fp8" if fp8 else "bf16"),
+                        new_cond_at=int(rng.integers(0, n_sink + W + 2)), new_cond_rows=new_rows,
+                        extra_rows=int(np.exp(rng.uniform(0.0, np.log(600.0))))))
+    return out
+
+
+QSWEEP = _sweep_cases()
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("kw", QSWEEP, ids=[c["spec"]["name"] for c in QSWEEP])
+def test_condition_queries_shape_sweep(kw):
+    """Seeded sweep: T log-uniform over 1 .. 399, 1 .. 599 extra query rows, a
+    condition replaced at a drawn chunk by a drawn number of rows (0 .. Lc),
+    one case in four fp8."""
+    spec = synthetic.small_spec(**kw["spec"])
+    run(spec, kw["new_cond_at"], kw["new_cond_rows"], kw["extra_rows"])
