@@ -10,7 +10,7 @@ import pytest
 import synthetic
 from oracle.cache import CacheModel
 from oracle.stream import attend_chunk
-from streams import BF16_MAX_ABS, BF16_REL_L2, FP8_REL_L2, LSE_TOL, dequant, errors, from_dev, say, to_dev
+from streams import BF16_MAX_ABS, BF16_REL_L2, FP8_LSE_TOL, FP8_REL_L2, LSE_TOL, dequant, errors, from_dev, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -22,6 +22,7 @@ def _check(og, lg, ref, ref_lse, fp8, what):
     assert np.isfinite(og).all(), what
     if fp8:
         assert rl <= FP8_REL_L2, (what, rl)
+        assert le <= FP8_LSE_TOL, (what, le)
     else:
         assert ma <= BF16_MAX_ABS and rl <= BF16_REL_L2, (what, ma, rl)
         assert le <= LSE_TOL, (what, le)
