@@ -516,9 +516,9 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
         constexpr int NM = NS + (DO_PV ? 2 * C::KB * C::DB : 0);  // PV: (kb, h2) outer, dim block inner
         constexpr int RA = 6;
         if (!wave_active) return;
-        // The MFMA wave runs this phase at a raised priority: when both waves of
-        // a SIMD have an instruction ready, its operand reads and MFMAs go first
-        // and the other wave's VALU work fills the gaps (about 2 % faster).
+        // Wave priorities steer the SIMD's arbiter when both waves have an
+        // instruction ready: the MFMA stream (operand reads, MFMAs) at 2 goes
+        // first; the row max after it drops to 0, below the softmax wave (1).
         __builtin_amdgcn_s_setprio(2);
         const uint32_t kofs = (uint32_t)uniform((j & 3) * C::TILE_B);
         const uint32_t vofs = (uint32_t)uniform(((j + 3) & 3) * C::TILE_B);
@@ -553,6 +553,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
           if (i + RA < NM) ring[i % RA] = rd(i + RA);
           __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
         if constexpr (DO_S) {
           const int valid = uniform(min(C::BN, ccur.len - ccur.off));
           if (valid < C::BN) mask_tail(sacc, valid);
@@ -564,11 +565,11 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
           }
           mx = max_halves(fmaxf(mx0, mx1)) * c;
         }
-        __builtin_amdgcn_s_setprio(0);
       };
       // Y: the loads of tile j + 2 and the softmax of S(j) -> P(j).
       // Returns whether loads were issued.
       auto phase_y = [&](int j) -> bool {
+        __builtin_amdgcn_s_setprio(1);  // above the MFMA wave's row max
         bool issued = false;
         if (j + 2 < n) {
           lcur = advance(lcur);
@@ -610,6 +611,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
           l_run += rs[0] + rs[1];
         }
         ccur = advance(ccur);
+        __builtin_amdgcn_s_setprio(0);
         return issued;
       };
       // barriers: group A waits for its own loads at the end of its Y phases,
