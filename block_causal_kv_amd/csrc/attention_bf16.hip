@@ -366,7 +366,10 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
         return;
       }
       const uint8_t* kl = lds + BUF * C::TILE_B;
-      // ---- S^T = K . Q^T
+      // ---- S^T = K . Q^T, at wave priority 2: the waves of a SIMD (here from
+      // different workgroups, not kept in step) then favour a wave streaming
+      // these MFMAs over one in its softmax (1-2.5 % faster than equal priority)
+      __builtin_amdgcn_s_setprio(2);
       f32x16 sacc[C::KB];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
@@ -382,6 +385,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
           if (kb == C::KB - 1 && more && ds % (C::DS / (2 * C::LPW)) == 0)
             load_one(nplan, ds / (C::DS / (2 * C::LPW)));
         }
+      __builtin_amdgcn_s_setprio(1);
       if (valid < C::BN) mask_tail(sacc, valid);
       // ---- online softmax
       bf16x8 pb[C::KB][2];  // P^T operands: [32-key block][16-key half]
@@ -433,6 +437,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
           }
       }
       l_run += rs;
+      __builtin_amdgcn_s_setprio(0);
     };
 
     // A unit of the split round takes its key tiles cyclically from tile rot
