@@ -519,7 +519,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
         constexpr bool DO_S = decltype(do_s)::value, DO_PV = decltype(do_pv)::value;
         constexpr int NS = DO_S ? C::KB * C::DS : 0;              // S: k-step outer, key block inner
         constexpr int NM = NS + (DO_PV ? 2 * C::KB * C::DB : 0);  // PV: (kb, h2) outer, dim block inner
-        constexpr int RA = 6;
+        constexpr int RA = 4;
         if (!wave_active) return;
         // Wave priorities steer the SIMD's arbiter when both waves have an
         // instruction ready: the MFMA stream (operand reads, MFMAs) at 2 goes
