@@ -86,6 +86,24 @@ def measured_traffic(config: str, launch_config: int):
     return None if e is None else e.get("hbm_bytes_per_launch")
 
 
+def host_cpu() -> dict:
+    """Logical CPUs this process may run on and the CPU model name."""
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        nproc = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": nproc, "cpu_model": model}
+
+
 def cpu_baseline(spec: synthetic.StreamSpec, budget_s: float = 12.0) -> dict:
     """Time the oracle on one steady-state call (chunk c = n_sink + W, whose
     concatenated sequence is exactly the resident set), one head at a time,
@@ -96,6 +114,7 @@ def cpu_baseline(spec: synthetic.StreamSpec, budget_s: float = 12.0) -> dict:
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
+    host = host_cpu()
     c = spec.n_sink + spec.window
     ck, cv = synthetic.cond_inputs(spec)
     clean = {j: synthetic.chunk_inputs(spec, j, clean_only=True) for j in range(c)}
@@ -113,6 +132,7 @@ def cpu_baseline(spec: synthetic.StreamSpec, budget_s: float = 12.0) -> dict:
     dt = time.perf_counter() - t0
     flop = 4.0 * done_heads * spec.chunk_tokens * nkv * spec.head_dim
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "threads": int(threads), "nproc": host["nproc"], "cpu_model": host["cpu_model"],
             "sample": "oracle (numpy fp64, explicit mask over [cond | chunks 0..%d]) on chunk %d, "
                       "step 1, %d of %d heads, all %d query rows: %.1f s; ms per chunk-step "
                       "equivalent %.0f" % (c, c, done_heads, spec.heads, spec.chunk_tokens, dt,

@@ -1,4 +1,4 @@
-"""ctypes declarations of libkvc.so (include/kvc.h).  Argument marshalling only."""
+"""ctypes declarations of libkvc.so (include/kvc.h, include/kvc_tools.h).  Argument marshalling only."""
 from __future__ import annotations
 
 import ctypes as C
@@ -6,7 +6,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvc.so")
 
-# Every symbol include/kvc.h declares, with (restype, argtypes).
+# Every symbol include/*.h declares, with (restype, argtypes).
 _I64P = C.POINTER(C.c_int64)
 _I32P = C.POINTER(C.c_int32)
 _IP = C.POINTER(C.c_int)

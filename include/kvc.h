@@ -72,7 +72,7 @@ const char* kvc_last_error(void);
  * Pool rows: the condition rows [0, Lc), then slot s (s < n_sink + W) at
  * round8(Lc) + s * round8(T) (round8 = round up to a multiple of 8; padding rows
  * stay zero), then one spare slot for the current chunk.  K is stored
- * row-major per head, V transposed per head (see kv_cache_pool_view); fp8
+ * row-major per head, V transposed per head (kv_cache_pool_view in kvc_tools.h); fp8
  * caches hold 1-byte codes plus one scale per (head, chunk).  No device memory
  * is allocated by any later call.  Errors: INVALID (also: a head's pool would
  * exceed 2^31 bytes), UNSUPPORTED, OOM (nothing allocated, *out untouched), HIP.
@@ -102,8 +102,8 @@ int kv_cache_create_layers(int chunk_tokens, int window_w, int n_sink, int cond_
  * call, owned by the cache and freed with it; kv_cache_destroy rejects it).
  * Every attention call (sink_window_attention, _rows, _chunks, autotune and
  * the configuration calls), kv_cache_set_condition(_rows) (this layer's
- * condition, [H][n][D]), kv_cache_write_chunk, kv_cache_query and
- * kv_cache_pool_view work on a view; appends, evictions and resets go
+ * condition, [H][n][D]), kv_cache_write_chunk and kv_cache_query work on
+ * a view (kv_cache_pool_view of kvc_tools.h too); appends, evictions and resets go
  * through the cache (STATE otherwise).
  * Errors: INVALID (not a cache handle, layer out of range), OOM.
  */
@@ -293,36 +293,6 @@ int kv_cache_set_config(kvc_handle h, int id);
 int kv_cache_get_config(kvc_handle h, int* out_id);
 int kv_cache_autotune(kvc_handle h, const void* q, const void* k_cur, const void* v_cur, void* o, int reps,
                       void* stream, int* out_id, float* out_ms);
-
-/*
- * Measurement probes (not part of the method).  kvc_probe_mfma_bf16 runs
- * `blocks` workgroups of 4 waves, each wave issuing iters x 4 independent
- * v_mfma_f32_32x32x16_bf16 (32768 FLOP each), and writes one float per
- * thread to the device array sink [blocks * 256]: the sustained rate of the
- * attention kernel's MFMA on this device.  kvc_probe_copy copies `bytes`
- * (a multiple of 16) from src to dst (device pointers) with 16-byte loads and
- * stores.  Both are asynchronous on `stream`; the caller times them.
- * Errors: INVALID, HIP.
- */
-int kvc_probe_mfma_bf16(float* sink, int blocks, int iters, void* stream);
-int kvc_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
-
-/*
- * kv_cache_pool_view - device addresses of the pool, for inspection (tests,
- * tools).  Read-only use; valid until destroy.  Any output may be NULL.
- *   rows     pool rows including the spare slot: round8(Lc) + (n_sink + W + 1) *
- *            round8(T); slot s starts at row round8(Lc) + s * round8(T), the spare
- *            slot (the current chunk of the last attention call) at rows - round8(T)
- *   k_pool   bf16: K [H][rows - round8(T)][D] (no spare slot: the call reads k_cur).
- *            fp8: K codes [H][rows][D] (1 byte each)
- *   v_pool   bf16: V transposed, [H][D][rows].  fp8: V codes transposed, [H][D][rows]
- *   scales   fp8: float32 [2 (K, V)][H][blocks]; block 0 = condition rows,
- *            1 + s = slot s, blocks - 1 = the current chunk of the last
- *            attention call.  NULL for bf16.
- *   blocks   fp8: n_sink + W + 2; bf16: 0
- */
-int kv_cache_pool_view(kvc_handle h, const void** k_pool, const void** v_pool, const float** scales,
-                       int64_t* rows, int* blocks);
 
 /* ---------------------------------------------------------------------------
  * Host-only slot table: the same bookkeeping a cache handle owns, with no
