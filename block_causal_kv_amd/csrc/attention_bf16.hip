@@ -31,6 +31,19 @@
 //   sharing one load stream among 256 query rows (rather than two workgroups
 //   of 128 rows loading the same K/V separately) measured a few percent faster.
 //
+// Schedules of the key-tile loop (a launch configuration picks one)
+//   ping-pong (8 waves): two wave groups per SIMD pair in alternate phases,
+//     one streaming MFMAs while the other runs its softmax (the default);
+//   lockstep (4 waves, 2 or 3 workgroups per CU): every wave runs the same
+//     phase of the same tile;
+//   in-wave (8 or 4 waves): each wave pipelines its own work over 32-key
+//     blocks, issuing the MFMAs of S(b+1) and PV(b-1) one at a time with the
+//     softmax of block b between them.  In this form all eight waves read
+//     MFMA operands from LDS at once and the LDS command queue fills up
+//     (rocprofv3: SQ_LDS_CMD_FIFO_FULL 4.3 M against 510 for the ping-pong),
+//     so at 720p it trails the ping-pong by about 5 %; it is kept as a
+//     measured alternative.
+//
 // Work split
 //   Every unit (head, query tile) has the same number of key tiles.  Units
 //   that fill the CUs' workgroup slots in whole rounds run one per workgroup:
@@ -68,7 +81,9 @@
 // row max is raised only when a tile's max exceeds it by more than kRescaleSlack
 // (wave-uniform decision); otherwise the stale max is kept and exp2 values up
 // to 2^kRescaleSlack are accumulated.  The result is the same softmax; the
-// rescale of the output accumulators becomes rare.
+// rescale of the output accumulators becomes rare.  P is rounded to bf16 for
+// the PV product, and the row sum adds those same rounded values, so every
+// output row is a convex combination of V rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -82,8 +97,14 @@ namespace {
 
 using namespace dev;
 
-template <int D, int NW_>
+// Schedules of the key-tile loop (see the kernel).
+constexpr int kLockstep = 0;  // all waves run the same phase; two LDS buffers
+constexpr int kPingPong = 1;  // two wave groups in alternate phases (8 waves)
+constexpr int kInWave = 2;    // each wave pipelines its own MFMAs and softmax over 32-key blocks
+
+template <int D, int NW_, int SCHED_ = (NW_ == 8 ? kPingPong : kLockstep)>
 struct Cfg {
+  static constexpr int SCHED = SCHED_;
   static constexpr int NW = NW_;             // waves per workgroup
   static constexpr int NT = NW * 64;         // threads per workgroup
   static constexpr int ROWS = NW * 32;       // query rows per workgroup
@@ -93,13 +114,15 @@ struct Cfg {
   static constexpr int TILE_B = BN * RB;     // bytes of a K tile (= bytes of a V^T tile)
   static constexpr int VRB = BN * 2;         // bytes of a V^T tile row
   static constexpr int LPW = TILE_B / 1024 / NW;  // 1 KB direct loads per wave, per tensor
-  static constexpr bool PP = NW == 8;        // ping-pong schedule (two wave groups per SIMD pair)
-  static constexpr int NBUF = PP ? 4 : 2;    // tile buffers: K tiles first, then the V^T tiles
+  static constexpr bool PP = SCHED == kPingPong;
+  static constexpr bool IW = SCHED == kInWave;
+  static constexpr int NBUF = SCHED == kLockstep ? 2 : 4;  // tile buffers: K tiles first, then the V^T tiles
   static constexpr int DS = D / 16;          // MFMA k-steps over the head dim
   static constexpr int DB = D / 32;          // 32-wide output blocks over the head dim
   static constexpr int KB = BN / 32;         // 32-key blocks per tile
   static_assert(TILE_B % (1024 * NW) == 0, "tile must split into whole 1 KB loads per wave");
   static_assert(DS % (2 * LPW) == 0, "the next tile's loads are spread evenly over the k-steps of S^T");
+  static_assert(!PP || NW == 8, "the ping-pong pairs the waves s and s + 4 of one SIMD");
 };
 
 // Ranges of the flattened (unit, key tile) space: range r starts at
@@ -111,9 +134,9 @@ __device__ inline int range_of(int64_t g, int64_t total, int n) { return (int)((
 // the current chunk).  STREAM = true: the whole-stream form, every chunk c of
 // one input attends to the condition rows of the cache and to chunks
 // {0 .. n_sink-1} and {c-W .. c} of the same input (segments derived here).
-template <int D, int NW, int WGS, bool STREAM>
+template <int D, int NW, int WGS, int SCHED, bool STREAM>
 __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a) {
-  using C = Cfg<D, NW>;
+  using C = Cfg<D, NW, SCHED>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::NBUF * C::TILE_B];
 
   const int tid = threadIdx.x;
@@ -406,10 +429,11 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
           for (int k = 0; k < 16; ++k) oacc[db][k] *= alpha;
       }
       // P = exp2(s*c - m) as bf16; the row sum adds the same bf16 values that
-      // enter the PV product.  Block by 32-key block: the PV MFMAs of block kb
-      // are issued before the exponentials of block kb+1, which do not depend
-      // on them, so the wave's own VALU work runs beside its MFMAs.
-      float rs = 0.f;
+      // enter the PV product (dot product with (1, 1)).  Block by 32-key block:
+      // the PV MFMAs of block kb are issued before the exponentials of block
+      // kb+1, which do not depend on them, so the wave's own VALU work runs
+      // beside its MFMAs.
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
@@ -420,8 +444,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
             const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][h2 * 8 + 2 * k], c, -m_run));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][h2 * 8 + 2 * k + 1], c, -m_run));
             w[k] = pack_bf16(p0, p1);
-            rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[k]),
-                                                 __builtin_bit_cast(bf16x2, 0x3f803f80u), rs, false);
+            rs[2 * h2 + (k & 1)] = sum2_bf16(w[k], rs[2 * h2 + (k & 1)]);
           }
           const u32x4 wv = {w[0], w[1], w[2], w[3]};
           pb[kb][h2] = __builtin_bit_cast(bf16x8, wv);
@@ -436,7 +459,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
                                                                 oacc[db], 0, 0, 0);
           }
       }
-      l_run += rs;
+      l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
       __builtin_amdgcn_s_setprio(0);
     };
 
@@ -595,8 +618,14 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
               for (int k = 0; k < 16; ++k) oacc[db][k] *= alpha;
           }
           // P = exp2(s*c - m) as bf16; the row sum adds the same bf16 values
-          // that enter the PV product (two independent chains)
-          float rs[2] = {0.f, 0.f};
+          // that enter the PV product (dot product with (1, 1), four
+          // independent chains).  The dot product waits for the MFMA pipe when
+          // the other wave of the SIMD streams MFMAs back to back (a probe
+          // measured about 70 cycles instead of 5.5), but in this schedule it
+          // finds the gaps between that wave's MFMAs: summing the widened
+          // values with plain adds instead (three times the instructions)
+          // measured 3 % slower.
+          float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -607,13 +636,12 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][h2 * 8 + 2 * k], c, -m_run));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][h2 * 8 + 2 * k + 1], c, -m_run));
                 w[k] = pack_bf16(p0, p1);
-                rs[h2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[k]),
-                                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), rs[h2], false);
+                rs[2 * h2 + (k & 1)] = sum2_bf16(w[k], rs[2 * h2 + (k & 1)]);
               }
               const u32x4 wv = {w[0], w[1], w[2], w[3]};
               pb[kb][h2] = __builtin_bit_cast(bf16x8, wv);
             }
-          l_run += rs[0] + rs[1];
+          l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
         }
         ccur = advance(ccur);
         __builtin_amdgcn_s_setprio(0);
@@ -645,6 +673,232 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
       phase_x(std::false_type(), std::true_type(), n);
       end_x();
       if (grp == 0) __syncthreads();  // group A's trailing phase
+    } else if constexpr (C::IW) {
+      // ---- in-wave software pipeline.  The tile's keys are taken in 32-key
+      // blocks b = 0 .. 2n-1 (block b is half b % 2 of tile b / 2).  Stage b
+      // issues the MFMAs of S(b+1) = K(b+1) Q^T and O^T += V(b-1)^T P(b-1)^T,
+      // one at a time, and between them the wave's own softmax of S(b) (row
+      // max, exponentials, bf16 P(b), row sum): the MFMAs run in the matrix
+      // pipe while the wave issues the softmax's VALU instructions, and the
+      // other wave of the SIMD fills the gaps of both.  S and P are double
+      // buffered by block parity.  Tile t lives in LDS buffer t % 4; its
+      // loads are issued in stage 2t - 4 (after the barrier that frees the
+      // buffer of tile t - 4, last read in stage 2t - 6), and each wave waits
+      // for its own loads of tile t before the barrier between stages 2t - 2
+      // and 2t - 1, the first stage that reads tile t.  No scalar memory
+      // access happens in the loop (segment bounds are cached in the cursor),
+      // so the operand reads can be awaited with partial LDS wait counts.
+      constexpr int RA = 4;  // LDS operand reads in flight
+      const int n = uniform(t1 - t0);  // key tiles of this item, >= 1
+      Cursor lcur = cur;               // the tile whose loads were issued last
+      {
+        const Plan p = make_plan(lcur, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * C::LPW; ++i) load_one(p, i);
+      }
+      if (n > 1) {
+        lcur = advance(lcur);
+        const Plan p = make_plan(lcur, 1);
+#pragma unroll
+        for (int i = 0; i < 2 * C::LPW; ++i) load_one(p, i);
+        __builtin_amdgcn_s_waitcnt((0x0F70 & ~0xF) | (2 * C::LPW));  // tile 0 done
+      } else {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
+      __syncthreads();
+      Cursor ccur = cur;      // the tile of the block whose softmax runs
+      f32x16 sc[2];           // S of the even / odd blocks
+      bf16x8 pb[2][2];        // P^T operands of the even / odd blocks, [16-key half]
+      float alpha = 1.f;      // rescale of O^T owed before the next PV MFMAs
+      bool owed = false;      // (wave-uniform)
+      // One stage.  PAR = parity of b; DO_S / DO_PV select the MFMA groups
+      // (absent at the two ends of the pipeline); SM: run the softmax of S(b).
+      // jb = tile of block b (its buffer is jb % 4).
+      // J4: jb % 4 when known at compile time (the steady loop is unrolled by
+      // four tiles, so the LDS buffer offsets become immediate offsets of the
+      // operand reads), else -1 (taken from jb at run time).
+      auto stage = [&](auto par_tag, auto s_tag, auto pv_tag, auto sm_tag, int jb, bool loads, auto j4_tag) {
+        constexpr int PAR = decltype(par_tag)::value;
+        constexpr bool DO_S = decltype(s_tag)::value, DO_PV = decltype(pv_tag)::value;
+        constexpr bool SM = decltype(sm_tag)::value;
+        constexpr int J4 = decltype(j4_tag)::value;
+        constexpr int NS = DO_S ? C::DS : 0;
+        constexpr int NP = DO_PV ? 2 * C::DB : 0;
+        constexpr int NM = NS + NP;
+        if (!wave_active) {
+          if (loads) {
+            lcur = advance(lcur);
+            const Plan p = make_plan(lcur, (jb + 2) & 3);
+#pragma unroll
+            for (int i = 0; i < 2 * C::LPW; ++i) load_one(p, i);
+          }
+          return;
+        }
+        // S(b+1): block 1 - PAR of tile jb + PAR; PV(b-1): block 1 - PAR of tile jb - 1 + PAR
+        const uint32_t kofs = J4 >= 0 ? (uint32_t)(((J4 + PAR) & 3) * C::TILE_B)
+                                      : (uint32_t)uniform(((jb + PAR) & 3) * C::TILE_B);
+        const uint32_t vofs = J4 >= 0 ? (uint32_t)(((J4 + 3 + PAR) & 3) * C::TILE_B)
+                                      : (uint32_t)uniform(((jb - 1 + PAR) & 3) * C::TILE_B);
+        // MFMA i: S and PV alternate while both run (the S chain then has an
+        // independent MFMA between its dependent ones)
+        auto is_s = [&](int i) { return NP == 0 || (NS > 0 && (i & 1) == 0 && i / 2 < NS); };
+        auto idx = [&](int i) { return NS == 0 || NP == 0 ? i : i / 2; };
+        auto rd = [&](int i) -> uint4 {
+          // (a lane's address lies below one tile and the buffer offset is a
+          // multiple of the tile size: the sum is the OR)
+          if (is_s(i)) {
+            const uint32_t a = kaddr[idx(i)] + (1 - PAR) * 32 * C::RB;
+            return *(const uint4*)(lds + (J4 >= 0 ? a + kofs : (a | kofs)));
+          }
+          const int q = idx(i), kh = q / C::DB, db = q % C::DB;
+          const uint32_t a = vaddr[2 * (1 - PAR) + kh];
+          return *(const uint4*)(lds + (J4 >= 0 ? a + vofs : (a | vofs)) + db * 32 * C::VRB);
+        };
+        auto mm = [&](int i, uint4 raw) {
+          const bf16x8 a_op = __builtin_bit_cast(bf16x8, raw);
+          if (is_s(i)) {
+            sc[1 - PAR] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_op, qreg[idx(i)], sc[1 - PAR], 0, 0, 0);
+          } else {
+            const int q = idx(i), kh = q / C::DB, db = q % C::DB;
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_op, pb[1 - PAR][kh], oacc[db], 0, 0, 0);
+          }
+        };
+        // the rescale owed from the previous stage, before this stage's PV MFMAs
+        if (DO_PV && owed) {
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int k = 0; k < 16; ++k) oacc[db][k] *= alpha;
+          owed = false;
+        }
+        if constexpr (DO_S) {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) sc[1 - PAR][k] = 0.f;
+        }
+        uint4 ring[RA];
+#pragma unroll
+        for (int i = 0; i < RA; ++i)
+          if (i < NM) ring[i] = rd(i);
+        Plan lp = {};
+        if (loads) {
+          lcur = advance(lcur);
+          lp = make_plan(lcur, (jb + 2) & 3);
+        }
+        float rs[4] = {0.f, 0.f, 0.f, 0.f};
+        unsigned w[8];
+        auto pair = [&](int k) {  // scores 2k, 2k + 1 of S(b) -> one dword of P(b)
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[PAR][2 * k], c, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[PAR][2 * k + 1], c, -m_run));
+          w[k] = pack_bf16(p0, p1);
+          rs[k & 3] = sum2_bf16(w[k], rs[k & 3]);
+        };
+        auto softmax_head = [&]() {  // mask, row max, lazy rescale of S(b)
+          const int vt = uniform(min(C::BN, ccur.len - ccur.off)) - 32 * PAR;  // valid keys of block b
+          if (vt < 32) {
+            const int lim = vt - 8 * hf;
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+              if (16 * (k >> 3) + (k & 7) >= lim) sc[PAR][k] = kNegInf;
+          }
+          float mx0 = kNegInf, mx1 = kNegInf;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            mx0 = fmaxf(mx0, sc[PAR][k]);
+            mx1 = fmaxf(mx1, sc[PAR][8 + k]);
+          }
+          const float mx = max_halves(fmaxf(mx0, mx1)) * c;
+          if (__any(mx > m_run + kRescaleSlack)) {
+            const float m_new = fmaxf(m_run, mx);
+            alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+            owed = true;
+          }
+        };
+        static_assert(NM > 0, "every stage issues MFMAs");
+        {
+#pragma unroll
+          for (int i = 0; i < NM; ++i) {
+            mm(i, ring[i % RA]);
+            if (i + RA < NM) ring[i % RA] = rd(i + RA);
+            if (loads) {
+#pragma unroll
+              for (int l = 0; l < 2 * C::LPW; ++l)
+                if (i == (l * NM) / (2 * C::LPW)) load_one(lp, l);
+            }
+            if constexpr (SM) {
+              if (i == 0) softmax_head();
+#pragma unroll
+              for (int k = 0; k < 8; ++k)
+                if (i == (NM > 1 ? 1 + (k * (NM - 1)) / 8 : 0)) pair(k);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        if constexpr (SM) {
+          const u32x4 w0 = {w[0], w[1], w[2], w[3]}, w1 = {w[4], w[5], w[6], w[7]};
+          pb[PAR][0] = __builtin_bit_cast(bf16x8, w0);
+          pb[PAR][1] = __builtin_bit_cast(bf16x8, w1);
+          l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+        }
+      };
+      using T0 = std::integral_constant<int, 0>;
+      using T1 = std::integral_constant<int, 1>;
+      using Y = std::true_type;
+      using N = std::false_type;
+      using JR = std::integral_constant<int, -1>;  // buffer taken from jb at run time
+      // Tile j is the pair of stages 2j (even: softmax of S(2j), S(2j+1) from
+      // tile j, PV(2j-1) from tile j-1, the loads of tile j+2 while j+2 < n)
+      // and 2j+1 (odd: softmax of S(2j+1), S(2j+2) from tile j+1, PV(2j) from
+      // tile j), with the barrier that makes tile j+1 visible between them.
+      // The first and last tiles are peeled so that the loop body has one
+      // shape (no runtime choice between stage forms, which made the compiler
+      // shuffle the accumulators between register assignments).
+      auto mid_barrier = [&](bool loads_in_flight) {
+        // tile j+1 complete for every wave; tile j+2's loads, just issued, may stay in flight
+        if (loads_in_flight)
+          __builtin_amdgcn_s_waitcnt((0x0F70 & ~0xF) | (2 * C::LPW));
+        else
+          __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+      };
+      stage(T1(), Y(), N(), N(), -1, false, JR());  // S(0) (stage "b = -1")
+      if (n == 1) {
+        stage(T0(), Y(), N(), Y(), 0, false, JR());
+      } else {
+        stage(T0(), Y(), N(), Y(), 0, n > 2, JR());
+        mid_barrier(n > 2);
+        stage(T1(), Y(), Y(), Y(), 0, false, JR());
+        ccur = advance(ccur);
+        int j = 1;
+        auto steady = [&](auto j4) {  // tile j (j % 4 = j4) with the loads of tile j + 2
+          stage(T0(), Y(), Y(), Y(), j, true, j4);
+          mid_barrier(true);
+          stage(T1(), Y(), Y(), Y(), j, false, j4);
+          ccur = advance(ccur);
+          ++j;
+        };
+        for (;;) {  // steady state, unrolled by four tiles (j starts at 1)
+          if (j + 2 >= n) break;
+          steady(std::integral_constant<int, 1>());
+          if (j + 2 >= n) break;
+          steady(std::integral_constant<int, 2>());
+          if (j + 2 >= n) break;
+          steady(std::integral_constant<int, 3>());
+          if (j + 2 >= n) break;
+          steady(std::integral_constant<int, 0>());
+        }
+        if (j + 1 < n) {  // j = n - 2: no loads left to issue
+          stage(T0(), Y(), Y(), Y(), j, false, JR());
+          mid_barrier(false);
+          stage(T1(), Y(), Y(), Y(), j, false, JR());
+          ccur = advance(ccur);
+          ++j;
+        }
+        stage(T0(), Y(), Y(), Y(), j, false, JR());  // j = n - 1
+      }
+      stage(T1(), N(), Y(), Y(), n - 1, false, JR());  // softmax of S(2n-1), PV(2n-2)
+      stage(T0(), N(), Y(), N(), n, false, JR());      // PV(2n-1)
     } else {
     // ---- main loop over key tiles [t0, t1), unrolled by two so each half reads
     // a fixed buffer.  At the top of a step the tile in buffer `buf` is complete
@@ -728,7 +982,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
 // merged in range order (deterministic).
 template <int D, int NW>
 __global__ __launch_bounds__(64) void merge_pieces_kernel(AttnArgs a) {
-  using C = Cfg<D, NW>;
+  using C = Cfg<D, NW, kLockstep>;
   constexpr int NR = C::DB * 16;
   const int unit = a.n_whole + (int)(blockIdx.x / NW);
   const int wave = (int)(blockIdx.x % NW), lane = threadIdx.x;
@@ -784,14 +1038,15 @@ __global__ __launch_bounds__(64) void merge_pieces_kernel(AttnArgs a) {
 // slots, and how many workgroups share one head's K/V stream), so callers
 // can measure them (kv_cache_autotune).
 struct LaunchCfg {
-  int waves, wgs;
+  int waves, wgs, sched;
 };
-constexpr LaunchCfg kCfg128[] = {{8, 1}, {4, 2}};
-constexpr LaunchCfg kCfg64[] = {{8, 1}, {4, 2}, {4, 3}};
+constexpr LaunchCfg kCfg128[] = {{8, 1, kPingPong}, {4, 2, kLockstep}, {8, 1, kInWave}, {4, 2, kInWave}};
+constexpr LaunchCfg kCfg64[] = {{8, 1, kPingPong}, {4, 2, kLockstep}, {4, 3, kLockstep}, {8, 1, kInWave},
+                                {4, 2, kInWave}};
 
-template <int D, int NW, int WGS>
+template <int D, int NW, int WGS, int SCHED>
 int launch_cfg(AttnArgs& a, hipStream_t stream) {
-  using C = Cfg<D, NW>;
+  using C = Cfg<D, NW, SCHED>;
   a.q_tiles = (a.Tq + C::ROWS - 1) / C::ROWS;
   a.q_rows = (a.Tq + a.q_tiles - 1) / a.q_tiles;  // equal tiles
   const int units = a.H * a.q_tiles;
@@ -835,7 +1090,7 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
   a.n_ranges = n_ranges;
   a.grid_whole = 8 * ((a.n_whole + 7) / 8);
   const int grid = a.grid_whole + 8 * ((a.n_ranges + 7) / 8);
-  hipLaunchKernelGGL((attention_bf16_kernel<D, NW, WGS, false>), dim3(grid), dim3(C::NT), 0, stream, a);
+  hipLaunchKernelGGL((attention_bf16_kernel<D, NW, WGS, SCHED, false>), dim3(grid), dim3(C::NT), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return -1;
   // ranges that are not exactly the last round's units split some of them
   if (n_ranges > 0 && n_ranges != rest) {
@@ -845,14 +1100,14 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
   return 0;
 }
 
-template <int D, int NW, int WGS>
+template <int D, int NW, int WGS, int SCHED>
 int launch_chunks(AttnArgs& a, hipStream_t stream) {
-  using C = Cfg<D, NW>;
+  using C = Cfg<D, NW, SCHED>;
   a.Tq = a.T;
   a.q_tiles = (a.T + C::ROWS - 1) / C::ROWS;
   a.q_rows = (a.T + a.q_tiles - 1) / a.q_tiles;  // equal tiles
   const int grid = a.H * a.n_chunks * a.q_tiles;
-  hipLaunchKernelGGL((attention_bf16_kernel<D, NW, WGS, true>), dim3(grid), dim3(C::NT), 0, stream, a);
+  hipLaunchKernelGGL((attention_bf16_kernel<D, NW, WGS, SCHED, true>), dim3(grid), dim3(C::NT), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -866,38 +1121,56 @@ size_t attention_ws_o_bytes(int num_cus, int head_dim) {
 }
 size_t attention_ws_ml_bytes(int num_cus) { return (size_t)2 * num_cus * 12 * 2 * 64 * sizeof(float); }
 
-int attention_bf16_configs(int head_dim, int* waves, int* wgs, int cap) {
+int attention_bf16_configs(int head_dim, int* waves, int* wgs, int* sched, int cap) {
   const LaunchCfg* t = head_dim == 128 ? kCfg128 : head_dim == 64 ? kCfg64 : nullptr;
-  const int n = head_dim == 128 ? 2 : head_dim == 64 ? 3 : 0;
+  const int n = head_dim == 128 ? (int)(sizeof kCfg128 / sizeof kCfg128[0])
+                : head_dim == 64 ? (int)(sizeof kCfg64 / sizeof kCfg64[0])
+                                 : 0;
   for (int i = 0; i < n && i < cap; ++i) {
     if (waves) waves[i] = t[i].waves;
     if (wgs) wgs[i] = t[i].wgs;
+    if (sched) sched[i] = t[i].sched;
   }
   return n;
 }
 
-int launch_attention_chunks_bf16(AttnArgs& a, int head_dim, int config, hipStream_t stream) {
+// Dispatch a launch configuration (an index into kCfg128 / kCfg64) to the
+// kernel instance of its (waves, workgroups per CU, schedule).
+template <template <int, int, int, int> class L>
+int dispatch(AttnArgs& a, int head_dim, int config, hipStream_t stream) {
   if (head_dim == 128) {
-    if (config == 0) return launch_chunks<128, 8, 1>(a, stream);
-    if (config == 1) return launch_chunks<128, 4, 2>(a, stream);
+    switch (config) {
+      case 0: return L<128, 8, 1, kCfg128[0].sched>::run(a, stream);
+      case 1: return L<128, 4, 2, kCfg128[1].sched>::run(a, stream);
+      case 2: return L<128, 8, 1, kCfg128[2].sched>::run(a, stream);
+      case 3: return L<128, 4, 2, kCfg128[3].sched>::run(a, stream);
+    }
   } else if (head_dim == 64) {
-    if (config == 0) return launch_chunks<64, 8, 1>(a, stream);
-    if (config == 1) return launch_chunks<64, 4, 2>(a, stream);
-    if (config == 2) return launch_chunks<64, 4, 3>(a, stream);
+    switch (config) {
+      case 0: return L<64, 8, 1, kCfg64[0].sched>::run(a, stream);
+      case 1: return L<64, 4, 2, kCfg64[1].sched>::run(a, stream);
+      case 2: return L<64, 4, 3, kCfg64[2].sched>::run(a, stream);
+      case 3: return L<64, 8, 1, kCfg64[3].sched>::run(a, stream);
+      case 4: return L<64, 4, 2, kCfg64[4].sched>::run(a, stream);
+    }
   }
   return -2;
 }
+template <int D, int NW, int WGS, int SCHED>
+struct CacheCall {
+  static int run(AttnArgs& a, hipStream_t s) { return launch_cfg<D, NW, WGS, SCHED>(a, s); }
+};
+template <int D, int NW, int WGS, int SCHED>
+struct StreamCall {
+  static int run(AttnArgs& a, hipStream_t s) { return launch_chunks<D, NW, WGS, SCHED>(a, s); }
+};
+
+int launch_attention_chunks_bf16(AttnArgs& a, int head_dim, int config, hipStream_t stream) {
+  return dispatch<StreamCall>(a, head_dim, config, stream);
+}
 
 int launch_attention_bf16(AttnArgs& a, int head_dim, int config, hipStream_t stream) {
-  if (head_dim == 128) {
-    if (config == 0) return launch_cfg<128, 8, 1>(a, stream);
-    if (config == 1) return launch_cfg<128, 4, 2>(a, stream);
-  } else if (head_dim == 64) {
-    if (config == 0) return launch_cfg<64, 8, 1>(a, stream);
-    if (config == 1) return launch_cfg<64, 4, 2>(a, stream);
-    if (config == 2) return launch_cfg<64, 4, 3>(a, stream);
-  }
-  return -2;
+  return dispatch<CacheCall>(a, head_dim, config, stream);
 }
 
 }  // namespace kvc

@@ -38,6 +38,12 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
 }
 
+// acc + the two bf16 values of a packed dword (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float sum2_bf16(unsigned w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3f803f80u), acc,
+                                         false);
+}
+
 __device__ __forceinline__ uint16_t f2bf(float x) {
   __bf16 b = (__bf16)x;  // round to nearest even
   return __builtin_bit_cast(uint16_t, b);

@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "../../include/kvc.h"
+#include "../../include/kvc_tools.h"
 #include "launch.h"
 #include "slot_table.h"
 
@@ -453,7 +454,7 @@ int sink_window_attention_rows(kvc_handle h, int n_q, const void* q, const void*
 }
 
 static int config_count(const kvc_cache* h) {
-  return h->kv_dtype == KVC_KV_FP8 ? 1 : kvc::attention_bf16_configs(h->D, nullptr, nullptr, 0);
+  return h->kv_dtype == KVC_KV_FP8 ? 1 : kvc::attention_bf16_configs(h->D, nullptr, nullptr, nullptr, 0);
 }
 
 int kv_cache_config_count(kvc_handle h, int* out_count) {
@@ -470,8 +471,8 @@ int kv_cache_config_info(kvc_handle h, int id, int* waves_per_workgroup, int* wo
   if (id < 0 || id >= n) return fail(KVC_ERR_INVALID, "kv_cache_config_info: config %d outside [0, %d)", id, n);
   int w = 8, g = 1;  // fp8: its one configuration
   if (h->kv_dtype != KVC_KV_FP8) {
-    int ws[8], gs[8];
-    kvc::attention_bf16_configs(h->D, ws, gs, 8);
+    int ws[16], gs[16];
+    kvc::attention_bf16_configs(h->D, ws, gs, nullptr, 16);
     w = ws[id];
     g = gs[id];
   }

@@ -72,9 +72,10 @@ struct AttnArgs {
 size_t attention_ws_o_bytes(int num_cus, int head_dim);
 size_t attention_ws_ml_bytes(int num_cus);
 // config: index into the launch configurations of the head dim (0 = default);
-// attention_bf16_configs lists them (waves per workgroup, workgroups per CU)
-// and returns their number.
-int attention_bf16_configs(int head_dim, int* waves, int* wgs, int cap);
+// attention_bf16_configs lists them (waves per workgroup, workgroups per CU,
+// schedule of the key-tile loop: 0 lockstep, 1 ping-pong, 2 in-wave
+// pipeline) and returns their number.
+int attention_bf16_configs(int head_dim, int* waves, int* wgs, int* sched, int cap);
 int launch_attention_bf16(AttnArgs& a, int head_dim, int config, hipStream_t stream);
 // Whole-stream form: every (head, chunk, query tile) of n_chunks chunks in one launch.
 int launch_attention_chunks_bf16(AttnArgs& a, int head_dim, int config, hipStream_t stream);

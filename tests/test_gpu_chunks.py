@@ -178,7 +178,7 @@ def _sweep_cases(n=16, seed=4048):
                         chunk_tokens=int(np.exp(rng.uniform(0.0, np.log(400.0)))), cond_len=int(rng.integers(0, 200)),
                         heads=int(rng.integers(1, 7)), head_dim=D, window=int(rng.integers(1, 6)),
                         n_sink=int(rng.integers(0, 3)), seed=300 + i, outlier_frac=0.01,
-                        config=int(rng.integers(0, 3 if D == 64 else 2))))
+                        config=int(rng.integers(0, 5 if D == 64 else 4))))
     return out
 
 

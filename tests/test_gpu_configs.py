@@ -10,8 +10,9 @@ from test_gpu_chunks import run_chunks
 
 pytestmark = pytest.mark.gpu
 
-# (head dim, configuration id): D = 128 has 2 configurations, D = 64 has 3
-CASES = [(128, 0), (128, 1), (64, 0), (64, 1), (64, 2)]
+# (head dim, configuration id): D = 128 has 4 configurations, D = 64 has 5
+N_CONFIGS = {128: 4, 64: 5}
+CASES = [(D, c) for D in (128, 64) for c in range(N_CONFIGS[D])]
 
 
 @pytest.mark.parametrize("D,cfg", CASES, ids=["d%d-c%d" % c for c in CASES])
@@ -40,10 +41,10 @@ def test_config_table_and_autotune():
                                 window=2, seed=60)
     H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
     cache = KVCache(T, spec.window, spec.n_sink, spec.cond_len, H, D)
-    assert cache.configs() == [(8, 1), (4, 2), (4, 3)]
+    assert cache.configs() == [(8, 1), (4, 2), (4, 3), (8, 1), (4, 2)]
     assert cache.config == 0
     with pytest.raises(KVCError) as e:
-        cache.config = 3
+        cache.config = 5
     assert e.value.code == _lib.KVC_ERR_INVALID
     ck, cv = synthetic.cond_inputs(spec)
     cache.set_condition(to_dev(ck), to_dev(cv))
@@ -55,13 +56,13 @@ def test_config_table_and_autotune():
     before = cache.query()
     best, ms = cache.autotune(q, k, v, reps=3)
     say("autotune: config %d, ms %s" % (best, ms))
-    assert 0 <= best < 3 and len(ms) == 3 and all(m > 0 for m in ms)
+    assert 0 <= best < 5 and len(ms) == 5 and all(m > 0 for m in ms)
     assert ms[best] == min(ms) or (best == 0 and min(ms) >= 0.98 * ms[0])
     assert cache.config == best
     assert cache.query() == before
     # every configuration gives the same result up to rounding order
     outs = []
-    for i in range(3):
+    for i in range(5):
         cache.config = i
         outs.append(cache.attention(q, k, v).float())
     torch.cuda.synchronize()
@@ -73,9 +74,9 @@ def test_config_table_and_autotune():
     f8.close()
 
 
-@pytest.mark.parametrize("cfg", [1])
+@pytest.mark.parametrize("cfg", [1, 2, 3])
 def test_whole_stream_other_config(cfg):
-    """The whole-stream form with the 4-wave configuration."""
+    """The whole-stream form with the other configurations."""
     from block_causal_kv_amd import KVCache
     spec = synthetic.small_spec("ragged_multi_c", n_chunks=5, chunk_tokens=604, cond_len=44, heads=6,
                                 head_dim=128, window=2, seed=61, outlier_frac=0.01)
