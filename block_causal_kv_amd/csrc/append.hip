@@ -72,7 +72,31 @@ __global__ __launch_bounds__(256) void transpose_v_kernel(const uint16_t* __rest
   }
 }
 
+// Fill n_spans byte spans (span i at base + i * stride + off, len bytes, both
+// even) with a repeated 16-bit pattern: the debug poisoning of freed slots.
+__global__ __launch_bounds__(256) void fill_spans_kernel(uint8_t* __restrict__ base, int64_t n_spans, int64_t stride,
+                                                         int64_t off, int64_t len, uint16_t pattern) {
+  const int64_t words = len / 2;
+  const int64_t total = n_spans * words;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t sp = i / words, w = i - sp * words;
+    *(uint16_t*)(base + sp * stride + off + 2 * w) = pattern;
+  }
+}
+
 }  // namespace
+
+int launch_fill_spans(void* base, int64_t n_spans, int64_t stride, int64_t off, int64_t len, uint16_t pattern,
+                      hipStream_t stream) {
+  if (n_spans <= 0 || len <= 0) return 0;
+  if ((len & 1) || (off & 1) || (stride & 1)) return -2;
+  const int64_t total = n_spans * (len / 2);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_spans_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (uint8_t*)base, n_spans, stride,
+                     off, len, pattern);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
 
 int launch_rows_copy_bf16(const uint16_t* src, uint16_t* pool, int H, int rows, int D, int64_t pool_rows,
                           int row0, hipStream_t stream) {

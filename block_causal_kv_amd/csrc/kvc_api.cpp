@@ -2,7 +2,7 @@
 // Argument validation, the device pool, the host slot table and kernel launches.
 // Every check happens before anything is enqueued, and a failed call leaves
 // the cache state unchanged.
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <cmath>
 #include <cstdarg>
@@ -52,13 +52,18 @@ struct kvc_cache {
   size_t k_bytes = 0, v_bytes = 0;
   float* scales = nullptr;    // fp8: [2][L*H][blocks]: block 0 = condition, 1 + s = slot s, last = current
   int scale_tensor = 0;       // fp8: L * H * blocks (offset of the V scales)
-  uint32_t* amax = nullptr;   // fp8: scratch of the quantiser, two buffers [2][L*H] used in turn
-  int amax_turn = 0;          // fp8 (root): the buffer the next quantisation uses (zeroed)
+  // fp8: maxima scratch of the quantiser, one region per (call site, layer)
+  // so that quantisations of different sites or layers may overlap on
+  // different streams (see amax_region); each region holds two buffers used
+  // in turn, the one not in use cleared by the quantiser for the next call.
+  uint32_t* amax = nullptr;
+  std::vector<int> amax_turn;  // root: the buffer the next quantisation of each region uses
   int blocks() const { return n_sink + W + 2; }
   int num_cus = 0;
   float* ws_o = nullptr;   // attention workspace: partials of split query tiles
   float* ws_ml = nullptr;
   int config = 0;  // bf16 attention launch configuration (kv_cache_set_config)
+  bool poison = false;  // debug: fill slots freed by kv_cache_evict / kv_cache_reset with NaN
   // Layers.  The root handle owns the pools, the slot table and the layer
   // views; a view (kv_cache_layer) points at its layer's heads in the pools.
   int layers = 1;
@@ -86,17 +91,48 @@ struct kvc_table {
 
 namespace {
 
-// fp8 cache: quantise K/V bf16 [H][rows][D] into pool rows [row0, row0 + rows) with scale block blk.
-int quantize_into(kvc_cache* h, const void* k, const void* v, int rows, int row0, int blk, hipStream_t st) {
+// Call sites of the fp8 quantiser.  Each (site, layer) pair, and each site's
+// all-layer writes through the cache handle, has its own scratch region, so
+// a chunk write of one layer on one stream may overlap an attention call of
+// another layer (or of the same layer) on another stream.
+enum AmaxSite { kSiteAttention = 0, kSiteChunk = 1, kSiteCondition = 2, kSites = 3 };
+
+// Words of the maxima scratch of a cache of L layers x H heads: per site, L
+// per-layer regions of 2 x 2H words and one all-layer region of 2 x 2HL.
+size_t amax_words(int H, int L) { return (size_t)kSites * 8 * H * L; }
+
+// Region (and its turn counter index) of a quantisation through handle h.
+void amax_region(kvc_cache* h, int site, uint32_t** base, int* words, int* turn_idx) {
   kvc_cache* r = h->top();
-  const int n = 2 * r->H * r->layers;  // words of one amax buffer
-  uint32_t* cur = r->amax + (size_t)r->amax_turn * n;
-  uint32_t* next = r->amax + (size_t)(1 - r->amax_turn) * n;
+  const size_t H = r->H, L = r->layers;
+  size_t off = (size_t)site * 8 * H * L;
+  if (h->root) {
+    off += (size_t)h->layer * 4 * H;
+    *words = (int)(2 * H);
+    *turn_idx = site * ((int)L + 1) + h->layer;
+  } else {
+    off += L * 4 * H;
+    *words = (int)(2 * H * L);
+    *turn_idx = site * ((int)L + 1) + (int)L;
+  }
+  *base = r->amax + off;
+}
+
+// fp8 cache: quantise K/V bf16 [H][rows][D] into pool rows [row0, row0 + rows) with scale block blk.
+int quantize_into(kvc_cache* h, const void* k, const void* v, int rows, int row0, int blk, int site,
+                  hipStream_t st) {
+  kvc_cache* r = h->top();
+  uint32_t* base;
+  int n, ti;
+  amax_region(h, site, &base, &n, &ti);
+  int& turn = r->amax_turn[ti];
+  uint32_t* cur = base + (size_t)turn * n;
+  uint32_t* next = base + (size_t)(1 - turn) * n;
   const int rc = kvc::launch_quantize_fp8((const uint16_t*)k, (const uint16_t*)v, h->heads_written(), rows, h->D,
                                           cur, next, n, (uint8_t*)h->k_pool, h->spare_rows * h->D,
                                           (uint8_t*)h->v_pool, h->spare_rows, row0, h->scales + blk,
                                           h->scale_tensor, h->blocks(), st);
-  if (rc == 0) r->amax_turn = 1 - r->amax_turn;
+  if (rc == 0) turn = 1 - turn;
   return rc;
 }
 
@@ -117,11 +153,109 @@ int write_chunk(kvc_cache* h, const void* k, const void* v, hipStream_t st, int*
   int64_t evicted;
   h->tbl().plan_append(&slot, &evicted);
   const int row0 = kvc::SlotTable::slot_row0(slot, h->T, h->Lc);
-  const int rc = h->kv_dtype == KVC_KV_FP8 ? quantize_into(h, k, v, h->T, row0, 1 + slot, st)
+  const int rc = h->kv_dtype == KVC_KV_FP8 ? quantize_into(h, k, v, h->T, row0, 1 + slot, kSiteChunk, st)
                                            : write_bf16(h, k, v, h->T, row0, st);
   if (out_slot) *out_slot = slot;
   if (out_evicted) *out_evicted = evicted;
   return rc;
+}
+
+// Debug poisoning (KVC_DEBUG_POISON set at create): the K rows and V^T
+// columns of a freed slot, every head of every layer, become NaN (bf16 0x7FC0,
+// E4M3 0x7F), so a kernel that still read a freed slot would show NaN in its
+// output.  Runs on the null stream between two device synchronisations.
+int poison_slot(kvc_cache* r, int slot) {
+  const bool fp8 = r->kv_dtype == KVC_KV_FP8;
+  const int64_t elem = fp8 ? 1 : 2;
+  const uint16_t pattern = fp8 ? 0x7F7F : 0x7FC0;
+  const int64_t heads = (int64_t)r->H * r->layers, D = r->D, T = r->T;
+  const int64_t row0 = kvc::SlotTable::slot_row0(slot, r->T, r->Lc);
+  if (hipDeviceSynchronize() != hipSuccess) return -1;
+  if (kvc::launch_fill_spans(r->k_pool, heads, (fp8 ? r->spare_rows : r->pool_rows) * D * elem, row0 * D * elem,
+                             T * D * elem, pattern, nullptr) != 0)
+    return -1;
+  if (kvc::launch_fill_spans(r->v_pool, heads * D, r->spare_rows * elem, row0 * elem, T * elem, pattern, nullptr) != 0)
+    return -1;
+  return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
+}
+
+// One attention call through handle h.
+int attention_call(kvc_cache* h, int n_q, const void* q, const void* k_cur, const void* v_cur, void* o, float* lse,
+                   float scale, void* stream, const char* who) {
+  if (!q || !k_cur || !v_cur || !o) return fail(KVC_ERR_INVALID, "%s: NULL q, k_cur, v_cur or o", who);
+  if (n_q < 1 || (int64_t)n_q * h->D * 2 > INT32_MAX || (int64_t)h->H * ((n_q + 255) / 256) > INT32_MAX)
+    return fail(KVC_ERR_INVALID, "%s: %d query rows (need 1 .. 32-bit offsets)", who, n_q);
+  if (!h->root && h->layers > 1)
+    return fail(KVC_ERR_STATE, "%s: a cache of %d layers attends through a layer view (kv_cache_layer)", who,
+                h->layers);
+  if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)h->D);
+  if (!std::isfinite(scale)) return fail(KVC_ERR_INVALID, "%s: scale not finite", who);
+  const bool fp8 = h->kv_dtype == KVC_KV_FP8;
+  float* ws_o = h->ws_o;
+  float* ws_ml = h->ws_ml;
+  kvc::AttnArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = (const uint16_t*)q;
+  a.kcur = (const uint16_t*)k_cur;
+  a.vcur = (const uint16_t*)v_cur;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.kpool = (const uint16_t*)h->k_pool;
+  a.vt = (const uint16_t*)h->v_pool;
+  a.rows_k = h->pool_rows;
+  a.rows_v = h->spare_rows;
+  a.cur_row0 = (int)h->pool_rows;
+  a.T = h->T;
+  a.Tq = n_q;
+  a.H = h->H;
+  a.c = scale * 1.4426950408889634f;
+  a.num_cus = h->num_cus;
+  a.ws_o = ws_o;
+  a.ws_ml = ws_ml;
+  hipStream_t st = (hipStream_t)stream;
+  if (fp8) {
+    // every chunk has its own scales: one segment per block, the current chunk
+    // quantised into the spare slot after the window slots
+    const std::vector<kvc::Segment> segs = h->tbl().segments(h->T, h->Lc, false, h->cond_rows());
+    if ((int)segs.size() + 1 > kvc::kMaxSegments) return fail(KVC_ERR_STATE, "%s: %zu segments", who, segs.size());
+    const int n_slots = h->n_sink + h->W;
+    const int cur_row0 = (int)h->pool_rows;
+    a.nseg = 0;
+    for (const kvc::Segment& sg : segs) {
+      a.seg_row0[a.nseg] = sg.row0;
+      a.seg_len[a.nseg] = sg.len;
+      a.seg_blk[a.nseg] =
+          sg.row0 < h->Lc ? 0 : 1 + (sg.row0 - kvc::SlotTable::round8(h->Lc)) / kvc::SlotTable::round8(h->T);
+      ++a.nseg;
+    }
+    a.seg_row0[a.nseg] = cur_row0;
+    a.seg_len[a.nseg] = h->T;
+    a.seg_blk[a.nseg] = n_slots + 1;
+    ++a.nseg;
+    a.k8 = (const uint8_t*)h->k_pool;
+    a.vt8 = (const uint8_t*)h->v_pool;
+    a.pool_rows8 = h->spare_rows;
+    a.scales = h->scales;
+    a.scale_tensor = h->scale_tensor;
+    a.scale_head = h->blocks();
+    const int rc = quantize_into(h, k_cur, v_cur, h->T, cur_row0, n_slots + 1, kSiteAttention, st);
+    if (rc != 0) return fail(KVC_ERR_HIP, "%s: quantise launch failed", who);
+    if (kvc::launch_attention_fp8(a, h->D, st) != 0) return fail(KVC_ERR_HIP, "%s: launch failed", who);
+    return KVC_OK;
+  }
+  const std::vector<kvc::Segment> segs = h->tbl().segments(h->T, h->Lc, true, h->cond_rows());
+  if ((int)segs.size() > kvc::kMaxSegments) return fail(KVC_ERR_STATE, "%s: %zu segments", who, segs.size());
+  a.nseg = (int)segs.size();
+  for (int i = 0; i < a.nseg; ++i) {
+    a.seg_row0[i] = segs[i].row0;
+    a.seg_len[i] = segs[i].len;
+  }
+  // the current chunk's V goes transposed into the spare slot, then the attention kernel
+  if (kvc::launch_transpose_v_bf16((const uint16_t*)v_cur, (uint16_t*)h->v_pool, h->H, h->T, h->D, h->spare_rows,
+                                   (int)h->pool_rows, st) != 0)
+    return fail(KVC_ERR_HIP, "%s: transpose launch failed", who);
+  if (kvc::launch_attention_bf16(a, h->D, h->config, st) != 0) return fail(KVC_ERR_HIP, "%s: launch failed", who);
+  return KVC_OK;
 }
 
 }  // namespace
@@ -191,8 +325,16 @@ int kv_cache_create_layers(int chunk_tokens, int window_w, int n_sink, int cond_
   e = hipMalloc(&c->k_pool, c->k_bytes);
   if (e == hipSuccess) e = hipMalloc(&c->v_pool, c->v_bytes);
   if (e == hipSuccess && fp8) e = hipMalloc(&c->scales, sizeof(float) * 2 * all_heads * c->blocks());
-  if (e == hipSuccess && fp8) e = hipMalloc(&c->amax, sizeof(uint32_t) * 4 * all_heads);
-  if (e == hipSuccess && fp8) e = hipMemset(c->amax, 0, sizeof(uint32_t) * 4 * all_heads);
+  if (fp8) {
+    try {
+      c->amax_turn.assign((size_t)kSites * (layers + 1), 0);
+    } catch (...) {
+      delete c;
+      return fail(KVC_ERR_OOM, "kv_cache_create: host allocation failed");
+    }
+  }
+  if (e == hipSuccess && fp8) e = hipMalloc(&c->amax, sizeof(uint32_t) * amax_words(heads, layers));
+  if (e == hipSuccess && fp8) e = hipMemset(c->amax, 0, sizeof(uint32_t) * amax_words(heads, layers));
   if (e == hipSuccess && fp8) e = hipMemset(c->scales, 0, sizeof(float) * 2 * all_heads * c->blocks());
   if (e == hipSuccess) e = hipMalloc(&c->ws_o, kvc::attention_ws_o_bytes(c->num_cus, head_dim));
   if (e == hipSuccess) e = hipMalloc(&c->ws_ml, kvc::attention_ws_ml_bytes(c->num_cus));
@@ -211,6 +353,8 @@ int kv_cache_create_layers(int chunk_tokens, int window_w, int n_sink, int cond_
                 "kv_cache_create: device allocation (pools of %zu + %zu bytes + workspace) failed: %s", kb, vb,
                 hipGetErrorString(e));
   }
+  const char* dbg = std::getenv("KVC_DEBUG_POISON");
+  c->poison = dbg != nullptr && dbg[0] != '\0' && std::strcmp(dbg, "0") != 0;
   *out = c;
   return KVC_OK;
 }
@@ -301,7 +445,8 @@ int kv_cache_set_condition_rows(kvc_handle h, int n, const void* k_cond, const v
     return fail(KVC_ERR_INVALID, "kv_cache_set_condition_rows: fp8 caches need n a multiple of 16 (got %d)", n);
   if (n > 0 && (!k_cond || !v_cond)) return fail(KVC_ERR_INVALID, "kv_cache_set_condition_rows: NULL K or V");
   if (n > 0) {
-    const int rc = h->kv_dtype == KVC_KV_FP8 ? quantize_into(h, k_cond, v_cond, n, 0, 0, (hipStream_t)stream)
+    const int rc = h->kv_dtype == KVC_KV_FP8 ? quantize_into(h, k_cond, v_cond, n, 0, 0, kSiteCondition,
+                                                             (hipStream_t)stream)
                                              : write_bf16(h, k_cond, v_cond, n, 0, (hipStream_t)stream);
     if (rc != 0) return fail(KVC_ERR_HIP, "kv_cache_set_condition_rows: launch failed");
   }
@@ -341,8 +486,14 @@ int kv_cache_evict(kvc_handle h, int n, int64_t* out_ids, int* out_n) {
   if (n > h->table.window_count())
     return fail(KVC_ERR_STATE, "kv_cache_evict: %d requested, %d window chunks held", n,
                 h->table.window_count());
+  std::vector<int64_t> before;
+  if (h->poison)
+    for (int sl = 0; sl < h->table.n_slots(); ++sl) before.push_back(h->table.slot_chunk(sl));
   h->table.evict(n, out_ids);
   if (out_n) *out_n = n;
+  for (size_t sl = 0; sl < before.size(); ++sl)
+    if (before[sl] >= 0 && h->table.slot_chunk((int)sl) < 0 && poison_slot(h, (int)sl) != 0)
+      return fail(KVC_ERR_HIP, "kv_cache_evict: poisoning the freed slot %zu failed (the chunks are evicted)", sl);
   return KVC_OK;
 }
 
@@ -350,7 +501,14 @@ int kv_cache_reset(kvc_handle h) {
   g_last_error.clear();
   if (!h) return fail(KVC_ERR_INVALID, "kv_cache_reset: handle is NULL");
   if (h->root) return fail(KVC_ERR_STATE, "kv_cache_reset: reset through the cache, not a layer view");
+  std::vector<int> freed;
+  if (h->poison)
+    for (int sl = 0; sl < h->table.n_slots(); ++sl)
+      if (h->table.slot_chunk(sl) >= 0) freed.push_back(sl);
   h->table.reset();
+  for (int sl : freed)
+    if (poison_slot(h, sl) != 0)
+      return fail(KVC_ERR_HIP, "kv_cache_reset: poisoning the freed slot %d failed (the cache is reset)", sl);
   return KVC_OK;
 }
 
@@ -377,80 +535,7 @@ int sink_window_attention_rows(kvc_handle h, int n_q, const void* q, const void*
                                void* o, float* lse, float scale, void* stream) {
   g_last_error.clear();
   if (!h) return fail(KVC_ERR_INVALID, "sink_window_attention: handle is NULL");
-  if (!q || !k_cur || !v_cur || !o)
-    return fail(KVC_ERR_INVALID, "sink_window_attention: NULL q, k_cur, v_cur or o");
-  if (n_q < 1 || (int64_t)n_q * h->D * 2 > INT32_MAX || (int64_t)h->H * ((n_q + 255) / 256) > INT32_MAX)
-    return fail(KVC_ERR_INVALID, "sink_window_attention: %d query rows (need 1 .. 32-bit offsets)", n_q);
-  if (!h->root && h->layers > 1)
-    return fail(KVC_ERR_STATE, "sink_window_attention: a cache of %d layers attends through a layer view "
-                "(kv_cache_layer)", h->layers);
-  if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)h->D);
-  if (!std::isfinite(scale)) return fail(KVC_ERR_INVALID, "sink_window_attention: scale not finite");
-  kvc::AttnArgs a;
-  std::memset(&a, 0, sizeof a);
-  a.q = (const uint16_t*)q;
-  a.kcur = (const uint16_t*)k_cur;
-  a.vcur = (const uint16_t*)v_cur;
-  a.o = (uint16_t*)o;
-  a.lse = lse;
-  a.kpool = (const uint16_t*)h->k_pool;
-  a.vt = (const uint16_t*)h->v_pool;
-  a.rows_k = h->pool_rows;
-  a.rows_v = h->spare_rows;
-  a.cur_row0 = (int)h->pool_rows;
-  a.T = h->T;
-  a.Tq = n_q;
-  a.H = h->H;
-  a.c = scale * 1.4426950408889634f;
-  a.num_cus = h->num_cus;
-  a.ws_o = h->ws_o;
-  a.ws_ml = h->ws_ml;
-  if (h->kv_dtype == KVC_KV_FP8) {
-    // every chunk has its own scales: one segment per block, the current chunk
-    // quantised into the spare slot after the window slots
-    const std::vector<kvc::Segment> segs = h->tbl().segments(h->T, h->Lc, false, h->cond_rows());
-    if ((int)segs.size() + 1 > kvc::kMaxSegments)
-      return fail(KVC_ERR_STATE, "sink_window_attention: %zu segments", segs.size());
-    const int n_slots = h->n_sink + h->W;
-    const int cur_row0 = (int)h->pool_rows;
-    a.nseg = 0;
-    for (const kvc::Segment& sg : segs) {
-      a.seg_row0[a.nseg] = sg.row0;
-      a.seg_len[a.nseg] = sg.len;
-      a.seg_blk[a.nseg] = sg.row0 < h->Lc ? 0 : 1 + (sg.row0 - kvc::SlotTable::round8(h->Lc)) / kvc::SlotTable::round8(h->T);
-      ++a.nseg;
-    }
-    a.seg_row0[a.nseg] = cur_row0;
-    a.seg_len[a.nseg] = h->T;
-    a.seg_blk[a.nseg] = n_slots + 1;
-    ++a.nseg;
-    a.k8 = (const uint8_t*)h->k_pool;
-    a.vt8 = (const uint8_t*)h->v_pool;
-    a.pool_rows8 = h->spare_rows;
-    a.scales = h->scales;
-    a.scale_tensor = h->scale_tensor;
-    a.scale_head = h->blocks();
-    if (quantize_into(h, k_cur, v_cur, h->T, cur_row0, n_slots + 1, (hipStream_t)stream) != 0)
-      return fail(KVC_ERR_HIP, "sink_window_attention: quantise launch failed");
-    if (kvc::launch_attention_fp8(a, h->D, (hipStream_t)stream) != 0)
-      return fail(KVC_ERR_HIP, "sink_window_attention: launch failed");
-    return KVC_OK;
-  }
-  const std::vector<kvc::Segment> segs = h->tbl().segments(h->T, h->Lc, true, h->cond_rows());
-  if ((int)segs.size() > kvc::kMaxSegments)
-    return fail(KVC_ERR_STATE, "sink_window_attention: %zu segments", segs.size());
-  a.nseg = (int)segs.size();
-  for (int i = 0; i < a.nseg; ++i) {
-    a.seg_row0[i] = segs[i].row0;
-    a.seg_len[i] = segs[i].len;
-  }
-  // the current chunk's V goes transposed into the spare slot, then the attention kernel
-  if (kvc::launch_transpose_v_bf16((const uint16_t*)v_cur, (uint16_t*)h->v_pool, h->H, h->T, h->D, h->spare_rows,
-                                   (int)h->pool_rows, (hipStream_t)stream) != 0)
-    return fail(KVC_ERR_HIP, "sink_window_attention: transpose launch failed");
-  if (kvc::launch_attention_bf16(a, h->D, h->config, (hipStream_t)stream) != 0)
-    return fail(KVC_ERR_HIP, "sink_window_attention: launch failed");
-  return KVC_OK;
+  return attention_call(h, n_q, q, k_cur, v_cur, o, lse, scale, stream, "sink_window_attention");
 }
 
 static int config_count(const kvc_cache* h) {

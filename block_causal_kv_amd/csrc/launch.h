@@ -1,11 +1,12 @@
 // Kernel launch interfaces shared by the C-ABI layer and the HIP kernels.
 #pragma once
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace kvc {
 
 constexpr int kMaxSegments = 66;  // condition + up to 64 slots + spare
+
 
 // Arguments of one attention call.  Segments are pool row ranges of one head
 // (the same for every head); the current chunk is handled after them.
@@ -90,6 +91,11 @@ int launch_rows_copy_bf16(const uint16_t* src, uint16_t* pool, int H, int rows, 
 // next multiple of 8 are written with zeros.
 int launch_transpose_v_bf16(const uint16_t* src, uint16_t* vt, int H, int rows, int D, int64_t vt_rows,
                             int col0, hipStream_t stream, int chunks = 1, int col_stride = 0);
+
+// Fill n_spans spans of len bytes (span i at base + i * stride + off; len, off
+// and stride even) with a repeated 16-bit pattern.
+int launch_fill_spans(void* base, int64_t n_spans, int64_t stride, int64_t off, int64_t len, uint16_t pattern,
+                      hipStream_t stream);
 
 // fp8 attention (E4M3 K/V codes, per-(head, chunk) scales).
 int launch_attention_fp8(AttnArgs& a, int head_dim, hipStream_t stream);
