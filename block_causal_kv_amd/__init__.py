@@ -159,6 +159,25 @@ class KVCache:
             check(self._lib.sink_window_attention_rows(self._h, n_q, qp, kp, vp, op, lp, C.c_float(scale), st))
         return out
 
+    def attention_noalloc(self, q, k_cur, v_cur, out=None, lse=None, scale: float = 0.0, stream=None):
+        """``sink_window_attention_noalloc``: as ``attention`` for the chunk's own
+        T query rows, with the kernels' scratch in the library's static device
+        array (for callers that cannot allocate); ``out`` must be given."""
+        import torch
+        qp = self._check(q, self.T, "q")
+        kp = self._check(k_cur, self.T, "k_cur")
+        vp = self._check(v_cur, self.T, "v_cur")
+        op = self._check(out, self.T, "out")
+        lp = None
+        if lse is not None:
+            if not lse.is_cuda or lse.dtype != torch.float32 or not lse.is_contiguous() \
+                    or tuple(lse.shape) != (self.H, self.T):
+                raise ValueError("lse must be a contiguous float32 CUDA tensor [H, T]")
+            lp = C.c_void_p(lse.data_ptr())
+        check(self._lib.sink_window_attention_noalloc(self._h, qp, kp, vp, op, lp, C.c_float(scale),
+                                                      C.c_void_p(_stream_ptr(stream))))
+        return out
+
     # ---- launch configurations of the attention kernel
     def configs(self) -> List[Tuple[int, int]]:
         """(waves per workgroup, workgroups per CU) of each configuration."""

@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvc.so")
-SOURCES = ["attention_bf16.hip", "attention_fp8.hip", "quant_fp8.hip", "append.hip", "probes.hip",
+SOURCES = ["attention_bf16.hip", "attention_fp8.hip", "quant_fp8.hip", "append.hip", "probes.hip", "scratch.hip",
            "kvc_api.cpp", "slot_table.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -179,9 +179,11 @@ int poison_slot(kvc_cache* r, int slot) {
   return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
 }
 
-// One attention call through handle h.
+// One attention call through handle h (sink_window_attention_rows and
+// sink_window_attention_noalloc).  noalloc: the split workspace and the fp8
+// maxima come from the library's static scratch array instead of the cache.
 int attention_call(kvc_cache* h, int n_q, const void* q, const void* k_cur, const void* v_cur, void* o, float* lse,
-                   float scale, void* stream, const char* who) {
+                   float scale, void* stream, bool noalloc, const char* who) {
   if (!q || !k_cur || !v_cur || !o) return fail(KVC_ERR_INVALID, "%s: NULL q, k_cur, v_cur or o", who);
   if (n_q < 1 || (int64_t)n_q * h->D * 2 > INT32_MAX || (int64_t)h->H * ((n_q + 255) / 256) > INT32_MAX)
     return fail(KVC_ERR_INVALID, "%s: %d query rows (need 1 .. 32-bit offsets)", who, n_q);
@@ -193,6 +195,25 @@ int attention_call(kvc_cache* h, int n_q, const void* q, const void* k_cur, cons
   const bool fp8 = h->kv_dtype == KVC_KV_FP8;
   float* ws_o = h->ws_o;
   float* ws_ml = h->ws_ml;
+  uint32_t* amax_cur = nullptr;
+  uint32_t* amax_next = nullptr;
+  if (noalloc) {
+    if (h->num_cus > kvc::kStaticScratchCUs)
+      return fail(KVC_ERR_UNSUPPORTED, "%s: the device has %d compute units; the static scratch holds the split "
+                  "workspace of at most %d", who, h->num_cus, kvc::kStaticScratchCUs);
+    if (fp8 && h->heads_written() > kvc::kStaticScratchHeads)
+      return fail(KVC_ERR_UNSUPPORTED, "%s: %d heads; the static scratch holds the fp8 maxima of at most %d", who,
+                  h->heads_written(), kvc::kStaticScratchHeads);
+    void* base = nullptr;
+    size_t bytes = 0;
+    if (kvc::static_scratch(&base, &bytes) != 0 || bytes < kvc::kStaticScratchBytes)
+      return fail(KVC_ERR_HIP, "%s: static scratch address lookup failed", who);
+    uint8_t* b = (uint8_t*)base;
+    ws_o = (float*)b;
+    ws_ml = (float*)(b + kvc::kStaticWsOBytes);
+    amax_cur = (uint32_t*)(b + kvc::kStaticWsOBytes + kvc::kStaticWsMlBytes);
+    amax_next = amax_cur + 2 * (size_t)h->heads_written();
+  }
   kvc::AttnArgs a;
   std::memset(&a, 0, sizeof a);
   a.q = (const uint16_t*)q;
@@ -238,7 +259,20 @@ int attention_call(kvc_cache* h, int n_q, const void* q, const void* k_cur, cons
     a.scales = h->scales;
     a.scale_tensor = h->scale_tensor;
     a.scale_head = h->blocks();
-    const int rc = quantize_into(h, k_cur, v_cur, h->T, cur_row0, n_slots + 1, kSiteAttention, st);
+    int rc;
+    if (noalloc) {
+      // the maxima start at zero: cleared here by a fill kernel (the array
+      // keeps whatever the last call left)
+      const int n = 2 * h->heads_written();
+      rc = kvc::launch_fill_spans(amax_cur, 1, 0, 0, (int64_t)n * 4, 0, st);
+      if (rc == 0)
+        rc = kvc::launch_quantize_fp8((const uint16_t*)k_cur, (const uint16_t*)v_cur, h->heads_written(), h->T, h->D,
+                                      amax_cur, amax_next, n, (uint8_t*)h->k_pool, h->spare_rows * h->D,
+                                      (uint8_t*)h->v_pool, h->spare_rows, cur_row0, h->scales + n_slots + 1,
+                                      h->scale_tensor, h->blocks(), st);
+    } else {
+      rc = quantize_into(h, k_cur, v_cur, h->T, cur_row0, n_slots + 1, kSiteAttention, st);
+    }
     if (rc != 0) return fail(KVC_ERR_HIP, "%s: quantise launch failed", who);
     if (kvc::launch_attention_fp8(a, h->D, st) != 0) return fail(KVC_ERR_HIP, "%s: launch failed", who);
     return KVC_OK;
@@ -535,7 +569,14 @@ int sink_window_attention_rows(kvc_handle h, int n_q, const void* q, const void*
                                void* o, float* lse, float scale, void* stream) {
   g_last_error.clear();
   if (!h) return fail(KVC_ERR_INVALID, "sink_window_attention: handle is NULL");
-  return attention_call(h, n_q, q, k_cur, v_cur, o, lse, scale, stream, "sink_window_attention");
+  return attention_call(h, n_q, q, k_cur, v_cur, o, lse, scale, stream, false, "sink_window_attention");
+}
+
+int sink_window_attention_noalloc(kvc_handle h, const void* q, const void* k_cur, const void* v_cur, void* o,
+                                  float* lse, float scale, void* stream) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "sink_window_attention_noalloc: handle is NULL");
+  return attention_call(h, h->T, q, k_cur, v_cur, o, lse, scale, stream, true, "sink_window_attention_noalloc");
 }
 
 static int config_count(const kvc_cache* h) {

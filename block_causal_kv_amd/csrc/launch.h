@@ -7,6 +7,16 @@ namespace kvc {
 
 constexpr int kMaxSegments = 66;  // condition + up to 64 slots + spare
 
+// Static scratch of the allocation-free attention entry point: the split
+// workspace of a device of up to kStaticScratchCUs compute units (partial O^T
+// and (max, sum) of two pieces per workgroup slot, head dim <= 128), then the
+// fp8 quantiser's maxima for up to kStaticScratchHeads heads.
+constexpr int kStaticScratchCUs = 256;
+constexpr int kStaticScratchHeads = 4096;
+constexpr size_t kStaticWsOBytes = (size_t)2 * kStaticScratchCUs * 8 * 4 * 16 * 64 * 4;  // 64 MiB
+constexpr size_t kStaticWsMlBytes = (size_t)2 * kStaticScratchCUs * 12 * 2 * 64 * 4;    // 1.5 MiB
+constexpr size_t kStaticAmaxBytes = (size_t)2 * 2 * kStaticScratchHeads * 4;             // 64 KiB
+constexpr size_t kStaticScratchBytes = kStaticWsOBytes + kStaticWsMlBytes + kStaticAmaxBytes;
 
 // Arguments of one attention call.  Segments are pool row ranges of one head
 // (the same for every head); the current chunk is handled after them.
@@ -96,6 +106,10 @@ int launch_transpose_v_bf16(const uint16_t* src, uint16_t* vt, int H, int rows, 
 // and stride even) with a repeated 16-bit pattern.
 int launch_fill_spans(void* base, int64_t n_spans, int64_t stride, int64_t off, int64_t len, uint16_t pattern,
                       hipStream_t stream);
+
+// Device address of this library's static scratch array on the current device
+// (looked up once per device); bytes receives its size.  Returns 0 or -1.
+int static_scratch(void** ptr, size_t* bytes);
 
 // fp8 attention (E4M3 K/V codes, per-(head, chunk) scales).
 int launch_attention_fp8(AttnArgs& a, int head_dim, hipStream_t stream);

@@ -217,6 +217,26 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
                           void* o, float* lse, float scale, void* stream);
 
 /*
+ * sink_window_attention_noalloc - sink_window_attention for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same kernels, with their
+ * scratch (partial results of split query tiles; the fp8 quantiser's maxima)
+ * taken from a static device array of the library instead of memory the cache
+ * allocated at create.  The call allocates nothing, HIP or otherwise.
+ *   q, k_cur, v_cur, o, lse, scale, stream: as sink_window_attention.
+ * The array (64 MiB + 1.5 MiB + 64 KiB) holds the split
+ * workspace of a device of at most 256 compute units and the fp8 maxima of at
+ * most 4096 heads; every GPU the library runs on keeps its own copy until the
+ * process ends, and its address is looked up on the first call on each device.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (other streams, other caches) race.  The maxima are cleared by a fill kernel
+ * at each call.  Errors: INVALID, STATE, HIP, UNSUPPORTED (more than 256
+ * compute units; an fp8 handle of more than 4096 heads).
+ */
+int sink_window_attention_noalloc(kvc_handle h, const void* q, const void* k_cur, const void* v_cur, void* o,
+                                  float* lse, float scale, void* stream);
+
+/*
  * sink_window_attention_rows - as sink_window_attention, for n_q query rows
  * that all see the key set of the chunk about to be generated: the condition
  * rows, every resident chunk and the current chunk (k_cur, v_cur [H][T][D]).
