@@ -70,13 +70,13 @@ def test_oversized_create_fails_with_oom_and_leaks_nothing():
     torch.cuda.synchronize()
     free0, total = torch.cuda.mem_get_info()
     h = C.c_void_p(0x1234)
-    # 1024 layers x 1024 heads of 1544 pool rows x D 128: ~0.8 TB
-    rc = lib.kv_cache_create_layers(8, 63, 1, 1024, 1024, 128, 0, 1024, C.byref(h))
+    # 1024 layers x 1024 heads, 1536 K rows and 1544 V rows of D 128 each: ~0.8 TB
+    # (T x heads x layers x D x 2 stays below 2^31, the limit checked before any allocation)
+    rc = lib.kv_cache_create_layers(4, 63, 1, 1024, 1024, 128, 0, 1024, C.byref(h))
     say("huge create:", rc, lib.kvc_last_error())
     assert rc == _lib.KVC_ERR_OOM
     assert h.value == 0x1234
     # K fits, V does not: the K pool allocated first must be released again
-    per_head = 2 * 128 * 2  # K or V bytes per pool row and head (bf16), x2 for the spare-slot-free K pool
     heads = 1024
     rows = int(0.6 * free0 / (heads * 128 * 2))
     lc = max(8, (rows - 2 * 8) // 8 * 8)
