@@ -200,6 +200,17 @@ class KVCache:
     def config(self, i: int) -> None:
         check(self._lib.kv_cache_set_config(self._h, int(i)))
 
+    @property
+    def split(self) -> int:
+        """Split form of a partly filled last round (``kv_cache_get_split``)."""
+        i = C.c_int()
+        check(self._lib.kv_cache_get_split(self._h, C.byref(i)))
+        return i.value
+
+    @split.setter
+    def split(self, form: int) -> None:
+        check(self._lib.kv_cache_set_split(self._h, int(form)))
+
     def autotune(self, q, k_cur, v_cur, out=None, reps: int = 5, stream=None) -> Tuple[int, List[float]]:
         """Time every configuration on this call (kv_cache_autotune) and keep
         the fastest; returns (chosen id, ms per call of each)."""

@@ -40,6 +40,8 @@ SIGNATURES = {
     "kv_cache_config_info": (C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_int), C.POINTER(C.c_int)]),
     "kv_cache_set_config": (C.c_int, [C.c_void_p, C.c_int]),
     "kv_cache_get_config": (C.c_int, [C.c_void_p, C.POINTER(C.c_int)]),
+    "kv_cache_set_split": (C.c_int, [C.c_void_p, C.c_int]),
+    "kv_cache_get_split": (C.c_int, [C.c_void_p, C.POINTER(C.c_int)]),
     "kv_cache_autotune": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int,
                                     C.c_void_p, C.POINTER(C.c_int), C.POINTER(C.c_float)]),
     "sink_window_attention_chunks": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,

@@ -1072,14 +1072,19 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
   int n_ranges = 0;
   if (rest > 0) {
     const int s = slots / rest;
-    const double aligned = 1.0 / s + (s > 1 ? 0.005 * s : 0.0);
-    const double unaligned = (double)rest / slots + 0.08;
-    const double whole = units > slots ? 1.0 : 1e30;  // (only when other rounds exist)
-    if (whole <= aligned && whole <= unaligned) {
-      rest = 0;
+    // a.split picks the form (measured by kv_cache_autotune); 0 = the cost model
+    int form = a.split;
+    if (form == 0) {
+      const double aligned = 1.0 / s + (s > 1 ? 0.005 * s : 0.0);
+      const double unaligned = (double)rest / slots + 0.08;
+      const double whole = units > slots ? 1.0 : 1e30;  // (only when other rounds exist)
+      form = whole <= aligned && whole <= unaligned ? 1 : aligned <= unaligned ? 2 : 3;
+    }
+    if (form == 1 || (form == 2 && s < 2)) {
+      rest = 0;  // the last round's units run whole
     } else {
       const int64_t total = (int64_t)rest * tiles;
-      n_ranges = aligned <= unaligned ? rest * s : slots;
+      n_ranges = form == 2 ? rest * s : slots;
       if (n_ranges > total) n_ranges = total >= 8 ? (int)(total & ~(int64_t)7) : (int)total;
     }
   }

@@ -87,9 +87,12 @@ __device__ __forceinline__ int swz_v8(int d) { return (d >> 2) & 3; }
 // MFMA row (lane column) -> key within a 32-key block (see header)
 __device__ __forceinline__ int krow8(int col) { return 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3); }
 
-// two floats -> two E4M3 codes in the low 16 bits (round to nearest even)
-__device__ __forceinline__ unsigned pk_fp8(float a, float b) {
-  return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+// four floats -> four E4M3 codes in one dword, a b in the low half, c d in
+// the high half (round to nearest even); the second conversion writes the
+// high half in place (word select), so no mask, shift or OR is needed
+__device__ __forceinline__ unsigned pk4_fp8(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
 template <int D>
@@ -170,13 +173,12 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
       for (int w = 0; w < 8; ++w) {
         const float y0 = qv[kk][4 * w] * inv, y1 = qv[kk][4 * w + 1] * inv;
         const float y2 = qv[kk][4 * w + 2] * inv, y3 = qv[kk][4 * w + 3] * inv;
-        const unsigned h01 = pk_fp8(y0, y1), h23 = pk_fp8(y2, y3);
-        hw[w] = h01 | (h23 << 16);
+        hw[w] = pk4_fp8(y0, y1, y2, y3);
         const float r0 = (y0 - __builtin_amdgcn_cvt_f32_fp8(hw[w], 0)) * 16.f;
         const float r1 = (y1 - __builtin_amdgcn_cvt_f32_fp8(hw[w], 1)) * 16.f;
         const float r2 = (y2 - __builtin_amdgcn_cvt_f32_fp8(hw[w], 2)) * 16.f;
         const float r3 = (y3 - __builtin_amdgcn_cvt_f32_fp8(hw[w], 3)) * 16.f;
-        lw[w] = pk_fp8(r0, r1) | (pk_fp8(r2, r3) << 16);
+        lw[w] = pk4_fp8(r0, r1, r2, r3);
       }
       const i32x8 hv = {(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3], (int)hw[4], (int)hw[5], (int)hw[6], (int)hw[7]};
       const i32x8 lv = {(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3], (int)lw[4], (int)lw[5], (int)lw[6], (int)lw[7]};
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
         const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 1], mult, bias));
         const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 2], mult, bias));
         const float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 3], mult, bias));
-        pw[kb * 4 + w] = pk_fp8(e0, e1) | (pk_fp8(e2, e3) << 16);
+        pw[kb * 4 + w] = pk4_fp8(e0, e1, e2, e3);
       }
     const i32x8 pv = {(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
     // ---- O^T += Vc^T . P8^T (one 64-key MFMA per 32 dims)
@@ -535,7 +537,7 @@ int launch_fp8(AttnArgs& a, hipStream_t stream) {
       slices = s;
     }
   }
-  if (slices > 1 && a.ws_o != nullptr) {
+  if (slices > 1 && a.ws_o != nullptr && a.split != 1) {
     a.rest = rest;
     a.slices = slices;
     a.n_whole = units - rest;

@@ -4,6 +4,7 @@
 // the cache state unchanged.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -63,6 +64,7 @@ struct kvc_cache {
   float* ws_o = nullptr;   // attention workspace: partials of split query tiles
   float* ws_ml = nullptr;
   int config = 0;  // bf16 attention launch configuration (kv_cache_set_config)
+  int split = 0;   // split of a partly filled last round of query tiles (kv_cache_set_split)
   bool poison = false;  // debug: fill slots freed by kv_cache_evict / kv_cache_reset with NaN
   // Layers.  The root handle owns the pools, the slot table and the layer
   // views; a view (kv_cache_layer) points at its layer's heads in the pools.
@@ -233,6 +235,7 @@ int attention_call(kvc_cache* h, int n_q, const void* q, const void* k_cur, cons
   a.num_cus = h->num_cus;
   a.ws_o = ws_o;
   a.ws_ml = ws_ml;
+  a.split = h->split;
   hipStream_t st = (hipStream_t)stream;
   if (fp8) {
     // every chunk has its own scales: one segment per block, the current chunk
@@ -429,6 +432,7 @@ int kv_cache_layer(kvc_handle h, int layer, kvc_handle* out_view) {
   v->device = h->device;
   v->num_cus = h->num_cus;
   v->config = h->config;
+  v->split = h->split;
   v->k_pool = (uint8_t*)h->k_pool + heads0 * h->D * (fp8 ? (size_t)h->spare_rows : (size_t)h->pool_rows * 2);
   v->v_pool = (uint8_t*)h->v_pool + heads0 * h->D * (size_t)h->spare_rows * (fp8 ? 1 : 2);
   v->scales = fp8 ? h->scales + heads0 * h->blocks() : nullptr;
@@ -623,6 +627,22 @@ int kv_cache_get_config(kvc_handle h, int* out_id) {
   return KVC_OK;
 }
 
+int kv_cache_set_split(kvc_handle h, int form) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "kv_cache_set_split: handle is NULL");
+  const int n = h->kv_dtype == KVC_KV_FP8 ? 2 : 4;
+  if (form < 0 || form >= n) return fail(KVC_ERR_INVALID, "kv_cache_set_split: form %d outside [0, %d)", form, n);
+  h->split = form;
+  return KVC_OK;
+}
+
+int kv_cache_get_split(kvc_handle h, int* out_form) {
+  g_last_error.clear();
+  if (!h || !out_form) return fail(KVC_ERR_INVALID, "kv_cache_get_split: NULL handle or output");
+  *out_form = h->split;
+  return KVC_OK;
+}
+
 int kv_cache_autotune(kvc_handle h, const void* q, const void* k_cur, const void* v_cur, void* o, int reps,
                       void* stream, int* out_id, float* out_ms) {
   g_last_error.clear();
@@ -630,21 +650,24 @@ int kv_cache_autotune(kvc_handle h, const void* q, const void* k_cur, const void
   if (reps < 1) return fail(KVC_ERR_INVALID, "kv_cache_autotune: reps = %d < 1", reps);
   if (!q || !k_cur || !v_cur || !o) return fail(KVC_ERR_INVALID, "kv_cache_autotune: NULL q, k_cur, v_cur or o");
   const int n = config_count(h);
-  const int before = h->config;
+  const int n_split = h->kv_dtype == KVC_KV_FP8 ? 2 : 4;
+  const int before = h->config, before_split = h->split;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
     if (e0) (void)hipEventDestroy(e0);
     return fail(KVC_ERR_HIP, "kv_cache_autotune: hipEventCreate failed");
   }
-  // Three rounds over the configurations, each timed once per round; a
-  // configuration's time is its best round, so a clock change during the
+  // Three rounds over every (configuration, split form), each timed once per
+  // round; a candidate's time is its best round, so a clock change during the
   // tuning does not favour whichever ran first.
   constexpr int kRounds = 3;
-  std::vector<float> ms_best(n, 0.f);
+  const int nc = n * n_split;
+  std::vector<float> ms_best(nc, 0.f);
   int rc = KVC_OK;
   for (int round = 0; round < kRounds && rc == KVC_OK; ++round) {
-    for (int id = 0; id < n && rc == KVC_OK; ++id) {
-      h->config = id;
+    for (int id = 0; id < nc && rc == KVC_OK; ++id) {
+      h->config = id / n_split;
+      h->split = id % n_split;
       rc = sink_window_attention(h, q, k_cur, v_cur, o, nullptr, 0.f, stream);  // warm-up
       if (rc != KVC_OK) break;
       if (hipEventRecord(e0, (hipStream_t)stream) != hipSuccess) {
@@ -664,24 +687,30 @@ int kv_cache_autotune(kvc_handle h, const void* q, const void* k_cur, const void
       if (round == 0 || ms < ms_best[id]) ms_best[id] = ms;
     }
   }
-  // the default (configuration 0) is kept unless another is at least 2 %
-  // faster: closer timings are within the run-to-run noise of one box
-  int best = before;
+  // the default (configuration 0, split by the cost model) is kept unless
+  // another candidate is at least 2 % faster: closer timings are within the
+  // run-to-run noise of one box
+  int best = 0;
   if (rc == KVC_OK) {
-    best = 0;
-    for (int id = 0; id < n; ++id) {
-      if (out_ms) out_ms[id] = ms_best[id];
+    for (int id = 0; id < nc; ++id)
       if (ms_best[id] < ms_best[best] * (best == 0 ? 0.98f : 1.f)) best = id;
-    }
+    if (out_ms)
+      for (int c = 0; c < n; ++c) {  // per configuration, its best split form
+        float m = ms_best[c * n_split];
+        for (int f = 1; f < n_split; ++f) m = std::min(m, ms_best[c * n_split + f]);
+        out_ms[c] = m;
+      }
   }
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
   if (rc != KVC_OK) {
     h->config = before;
+    h->split = before_split;
     return rc;
   }
-  h->config = best;
-  if (out_id) *out_id = best;
+  h->config = best / n_split;
+  h->split = best % n_split;
+  if (out_id) *out_id = h->config;
   return KVC_OK;
 }
 

@@ -44,6 +44,8 @@ struct AttnArgs {
   // n_ranges equal contiguous ranges, one per workgroup; a unit that
   // straddles ranges is computed in pieces.  Pieces and slices leave partial
   // results that a merge kernel, launched next on the same stream, combines.
+  int split;     // split of a partly filled last round: 0 by the cost model, 1 none (whole
+                 // units), 2 aligned slices, 3 one equal range per slot (fp8: 0 and 1 only)
   int tiles;     // key tiles of one unit (all segments + the current chunk)
   int n_whole;
   int rest;

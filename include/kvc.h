@@ -295,22 +295,32 @@ int kvc_chunks_workspace_bytes(kvc_handle h, int n_chunks, size_t* out_bytes);
  *                         configuration id.  Errors: INVALID (bad id).
  * kv_cache_set_config / kv_cache_get_config - the configuration later
  *                         attention calls use.  Errors: INVALID (bad id).
+ * kv_cache_set_split / kv_cache_get_split - how a partly filled last round
+ *   of (head, query tile) units is spread over the compute units: 0 by the
+ *   library's cost model (the default), 1 run whole (no split), 2 each unit
+ *   cut into equal key slices, 3 the round's (unit, key tile) space cut into
+ *   one equal range per workgroup slot.  fp8 caches: 0 and 1.  Pieces of a
+ *   split unit are merged by a second kernel.  Errors: INVALID.
  * kv_cache_autotune - run sink_window_attention on these inputs (the cache's
  *   current contents: call it at the state to tune for, e.g. a full window)
- *   with every configuration: three rounds over the configurations, each
- *   with one warm-up and `reps` timed calls per configuration (HIP events on
- *   `stream`; the call waits for them); a configuration's time is its best
- *   round, and the fastest is kept, except that configuration 0 stays unless
- *   another is at least 2 % faster.
+ *   with every (configuration, split form): three rounds over them, each
+ *   with one warm-up and `reps` timed calls per candidate (HIP events on
+ *   `stream`; the call waits for them); a candidate's time is its best
+ *   round, and the fastest is kept (configuration and split form), except
+ *   that configuration 0 with the cost model's split stays unless another
+ *   candidate is at least 2 % faster.
  *   o holds that last run's output (not necessarily the chosen
- *   configuration's).  out_ms (NULL or count floats) receives the mean time
- *   per call of each configuration.  The cache's slot table is unchanged.
- *   Errors: INVALID, HIP (the previous configuration is kept).
+ *   candidate's).  out_ms (NULL or count floats) receives, per
+ *   configuration, the mean time per call of its best split form.  The
+ *   cache's slot table is unchanged.  Errors: INVALID, HIP (the previous
+ *   configuration and split form are kept).
  */
 int kv_cache_config_count(kvc_handle h, int* out_count);
 int kv_cache_config_info(kvc_handle h, int id, int* waves_per_workgroup, int* workgroups_per_cu);
 int kv_cache_set_config(kvc_handle h, int id);
 int kv_cache_get_config(kvc_handle h, int* out_id);
+int kv_cache_set_split(kvc_handle h, int form);
+int kv_cache_get_split(kvc_handle h, int* out_form);
 int kv_cache_autotune(kvc_handle h, const void* q, const void* k_cur, const void* v_cur, void* o, int reps,
                       void* stream, int* out_id, float* out_ms);
 

@@ -60,10 +60,11 @@ def say(*a):
 def run_stream(spec: synthetic.StreamSpec, check: Iterable[int], rows: Optional[np.ndarray] = None,
                evict_plan: Optional[Dict[int, int]] = None,
                max_abs: float = BF16_MAX_ABS, rel_l2: float = BF16_REL_L2, lse_tol: float = LSE_TOL,
-               config: Optional[int] = None):
+               config: Optional[int] = None, split: Optional[int] = None):
     """Run chunks 0..max(check) of ``spec``; compare attention at the chunks in
     ``check`` (every step, the given rows or all) and every append's indices.
-    ``config`` selects the kernel's launch configuration."""
+    ``config`` selects the kernel's launch configuration, ``split`` the split
+    form of a partly filled last round of query tiles."""
     import torch
     from block_causal_kv_amd import KVCache
 
@@ -72,6 +73,8 @@ def run_stream(spec: synthetic.StreamSpec, check: Iterable[int], rows: Optional[
     cache = KVCache(T, spec.window, spec.n_sink, spec.cond_len, H, D, spec.kv_dtype)
     if config is not None:
         cache.config = config
+    if split is not None:
+        cache.split = split
     model = CacheModel(spec.window, spec.n_sink)
     ck, cv = synthetic.cond_inputs(spec)
     cache.set_condition(to_dev(ck), to_dev(cv))

@@ -34,6 +34,19 @@ def test_config_many_units(D, cfg):
     run_stream(spec, [0, 3], rows=rows, config=cfg)
 
 
+@pytest.mark.parametrize("kv_dtype,form", [("bf16", 1), ("bf16", 2), ("bf16", 3), ("fp8", 1)])
+def test_split_forms(kv_dtype, form):
+    """Each split form of a partly filled last round (whole units, aligned key
+    slices, one range per slot) against the oracle, on a stream whose units
+    fill more than one round."""
+    from block_causal_kv_amd import KVCache
+    spec = synthetic.small_spec("split%d_%s" % (form, kv_dtype), n_chunks=4, chunk_tokens=1104, cond_len=64,
+                                heads=96, head_dim=128, window=2, seed=55 + form, kv_dtype=kv_dtype)
+    rows = np.array(sorted(set(range(0, 1104, 41)) | set(range(1094, 1104))))
+    say("split form %d, %s" % (form, kv_dtype))
+    run_stream(spec, [0, 3], rows=rows, split=form)
+
+
 def test_config_table_and_autotune():
     import torch
     from block_causal_kv_amd import KVCache, KVCError, _lib
@@ -59,6 +72,7 @@ def test_config_table_and_autotune():
     assert 0 <= best < 5 and len(ms) == 5 and all(m > 0 for m in ms)
     assert ms[best] == min(ms) or (best == 0 and min(ms) >= 0.98 * ms[0])
     assert cache.config == best
+    assert 0 <= cache.split < 4
     assert cache.query() == before
     # every configuration gives the same result up to rounding order
     outs = []
