@@ -316,39 +316,11 @@ def whole_stream(args) -> int:
     return 0
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="720p", choices=["720p", "mid", "long", "fp8"])
-    ap.add_argument("--sets", type=int, default=4, help="distinct input sets cycled by step")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--flatness", action="store_true",
-                    help="stream the 300-chunk long config from an empty cache and report per-chunk "
-                         "latency flatness and device memory instead of the throughput line")
-    ap.add_argument("--no-probes", action="store_true",
-                    help="skip the MFMA and copy probes that report this device's sustained rates")
-    ap.add_argument("--no-autotune", action="store_true",
-                    help="keep the default launch configuration instead of timing each once before the run")
-    ap.add_argument("--chunks", type=int, default=0,
-                    help="time the whole-stream form instead: every chunk of an N-chunk stream in one call")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: attention shards by heads with no exchange, so "
-              "N GPUs would each run this same kernel on H/N heads; no multi-GPU run is made.",
-              file=sys.stderr)
-        return 2
-
+def measure_stream(spec: synthetic.StreamSpec, steps: int, warmup: int, n_sets: int, autotune: bool) -> dict:
+    """Time ``steps`` steady chunk-steps of ``spec`` (attention calls + clean
+    append) after ``warmup`` untimed ones; inputs resident in HBM first."""
     import torch
     from block_causal_kv_amd import KVCache
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-
-    if args.flatness:
-        return flatness(args)
-    if args.chunks > 0:
-        return whole_stream(args)
-    spec = synthetic.SPECS[args.config]
     H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
     dev = torch.device("cuda", 0)
 
@@ -359,7 +331,7 @@ def main() -> int:
     # ---- inputs resident in HBM before timing
     ck, cv = synthetic.cond_inputs(spec)
     sets = []
-    for i in range(args.sets):
+    for i in range(n_sets):
         x = synthetic.chunk_inputs(spec, i)
         sets.append({"q": [dev_bf16(a) for a in x.q], "k": [dev_bf16(a) for a in x.k],
                      "v": [dev_bf16(a) for a in x.v], "kc": dev_bf16(x.k_clean),
@@ -389,14 +361,14 @@ def main() -> int:
         cache.append_chunk(s["kc"], s["vc"], stream=stream)
     # launch configuration: measured on a steady-state call before the run
     tuned = None
-    if not args.no_autotune and spec.kv_dtype == "bf16":
+    if autotune and len(cache.configs()) > 1:
         s0 = sets[0]
         best, tms = cache.autotune(s0["q"][0], s0["k"][0], s0["v"][0], out=out, reps=5, stream=stream)
         tuned = {"chosen": best, "ms_per_config": [round(t, 4) for t in tms]}
     cfgs = cache.configs()
     kernel_cfg = {"id": cache.config, "waves_per_workgroup": cfgs[cache.config][0],
                   "workgroups_per_cu": cfgs[cache.config][1], "autotune": tuned}
-    for i in range(args.warmup):
+    for i in range(warmup):
         chunk_step(i)
     torch.cuda.synchronize()
     q = cache.query()
@@ -405,23 +377,64 @@ def main() -> int:
     evs = [([torch.cuda.Event(enable_timing=True) for _ in range(spec.steps)],
             [torch.cuda.Event(enable_timing=True) for _ in range(spec.steps)],
             torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+           for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         chunk_step(i, evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    res = {"elapsed": elapsed, "config": cache.config, "kernel_cfg": kernel_cfg,
+           "attn_ms": [e[0][s].elapsed_time(e[1][s]) for e in evs for s in range(spec.steps)],
+           "app_ms": [e[2].elapsed_time(e[3]) for e in evs], "stream": stream}
+    cache.close()
+    return res
 
-    attn_ms = [e[0][s].elapsed_time(e[1][s]) for e in evs for s in range(spec.steps)]
-    app_ms = [e[2].elapsed_time(e[3]) for e in evs]
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="720p", choices=["720p", "mid", "long", "fp8"])
+    ap.add_argument("--sets", type=int, default=4, help="distinct input sets cycled by step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flatness", action="store_true",
+                    help="stream the 300-chunk long config from an empty cache and report per-chunk "
+                         "latency flatness and device memory instead of the throughput line")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the MFMA and copy probes that report this device's sustained rates")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the fp8-cache run that the default 720p line reports beside the headline")
+    ap.add_argument("--no-autotune", action="store_true",
+                    help="keep the default launch configuration instead of timing each once before the run")
+    ap.add_argument("--chunks", type=int, default=0,
+                    help="time the whole-stream form instead: every chunk of an N-chunk stream in one call")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: attention shards by heads with no exchange, so "
+              "N GPUs would each run this same kernel on H/N heads; no multi-GPU run is made.",
+              file=sys.stderr)
+        return 2
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+    if args.flatness:
+        return flatness(args)
+    if args.chunks > 0:
+        return whole_stream(args)
+    spec = synthetic.SPECS[args.config]
+    H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
+    m = measure_stream(spec, args.steps, args.warmup, args.sets, not args.no_autotune)
+    stream, elapsed, kernel_cfg = m["stream"], m["elapsed"], m["kernel_cfg"]
+    attn_ms, app_ms = m["attn_ms"], m["app_ms"]
     ms_step = elapsed * 1e3 / args.steps
     fl_call = flop_per_call(spec)
     value = spec.steps * fl_call * args.steps / elapsed / 1e12
     attn_avg = float(np.mean(attn_ms))
     achieved = fl_call / (attn_avg * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if spec.kv_dtype == "fp8" else PEAK_BF16_TFLOPS
-    traffic = measured_traffic(args.config, cache.config) if spec.kv_dtype == "bf16" else None
+    traffic = measured_traffic(args.config, m["config"]) if spec.kv_dtype == "bf16" else None
     app_bytes = 2.0 * 2 * H * T * D * (1 if spec.kv_dtype == "fp8" else 2)  # K+V read and written
     rec = {
         "metric": METRIC,
@@ -450,6 +463,21 @@ def main() -> int:
                      "algorithmic_bytes_per_launch": bytes_per_call(spec),
                      "algorithmic_flop_per_launch": fl_call},
     }
+    if args.config == "720p" and not args.no_fp8:
+        # the same stream with an E4M3 cache (fp8 MFMA for both products),
+        # timed after the headline run; reported beside it
+        f8 = synthetic.SPECS["fp8"]
+        n8 = max(5, args.steps // 2)
+        m8 = measure_stream(f8, n8, args.warmup, args.sets, False)
+        a8 = float(np.mean(m8["attn_ms"]))
+        fl8 = flop_per_call(f8)
+        rec["fp8_kv"] = {"workload": workload_name(f8), "steps": n8,
+                         "ms_per_step": round(m8["elapsed"] * 1e3 / n8, 4),
+                         "attention_ms_per_call": round(a8, 4),
+                         "tflops_per_call": round(fl8 / (a8 * 1e-3) / 1e12, 2),
+                         "frac_of_fp8_peak": round(fl8 / (a8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+                         "speedup_vs_bf16_call": round(attn_avg / a8, 4),
+                         "append_ms": round(float(np.mean(m8["app_ms"])), 4)}
     peaks = measure_peaks(stream) if not args.no_probes else None  # after the timed region
     if peaks is not None:
         peaks["attention_frac_of_measured_mfma"] = round(achieved / peaks["bf16_mfma_tflops"], 4)
@@ -459,7 +487,6 @@ def main() -> int:
         rec["cpu_baseline"] = cpu_baseline(spec)
     else:
         rec["cpu_baseline"] = None
-    cache.close()
     print(json.dumps(rec), flush=True)
     return 0
 
