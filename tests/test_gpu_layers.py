@@ -203,3 +203,69 @@ def test_whole_stream_on_a_layer_view():
         ref, ref_lse = masked_attention(cat(qs), cat([conds[l][0]] + ks), cat([conds[l][1]] + vs), m, specs[l].scale)
         _check(from_dev(o), lse.cpu().numpy().astype(np.float64), ref, ref_lse, False, "layer %d whole stream" % l)
     cache.close()
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_layer_writes_overlap_next_layer_attention(kv_dtype):
+    """A multi-layer chunk-step as a model pipelines it: layer l's two attention
+    calls on stream A, then layer l's clean K/V written on stream B
+    (kv_cache_write_chunk, after an event of A) while layer l+1's attention
+    runs on A; one commit per chunk, the next chunk's attention after an event
+    of B.  In an fp8 cache both streams quantise at once (the layer write and
+    the attention call's own K/V), each in its own scratch; every layer of
+    every chunk against the oracle fed that layer's history."""
+    import torch
+    from block_causal_kv_amd import KVCache
+    L, T, Lc, H, D, W, n = 3, 96, 16, 2, 128, 2, 6
+    fp8 = kv_dtype == "fp8"
+    store = dequant if fp8 else (lambda x: x)
+    specs = [synthetic.small_spec("ovl%d" % l, n_chunks=n, chunk_tokens=T, cond_len=Lc, heads=H, head_dim=D,
+                                  window=W, steps=2, clean_from_last_step=False, seed=300 + l, outlier_frac=0.01,
+                                  kv_dtype=kv_dtype) for l in range(L)]
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    cache = KVCache(T, W, 1, Lc, H, D, kv_dtype, layers=L)
+    views = [cache.layer(l) for l in range(L)]
+    conds = [synthetic.cond_inputs(sp) for sp in specs]
+    sa.wait_stream(torch.cuda.current_stream())
+    for l in range(L):
+        views[l].set_condition(to_dev(conds[l][0]), to_dev(conds[l][1]), stream=sa)
+    model = CacheModel(W, 1)
+    keep, results = [], []
+    committed = None
+    for c in range(n):
+        xs = [synthetic.chunk_inputs(sp, c) for sp in specs]
+        dev = [[(to_dev(x.q[s]), to_dev(x.k[s]), to_dev(x.v[s])) for s in range(2)] for x in xs]
+        clean = [(to_dev(x.k_clean), to_dev(x.v_clean)) for x in xs]
+        sa.wait_stream(torch.cuda.current_stream())  # the input copies
+        sb.wait_stream(torch.cuda.current_stream())
+        if committed is not None:
+            sa.wait_event(committed)
+        outs = []
+        for l in range(L):
+            lo = []
+            for q, k, v in dev[l]:
+                lse = torch.empty((H, T), dtype=torch.float32, device="cuda")
+                lo.append((views[l].attention(q, k, v, lse=lse, stream=sa), lse))
+            outs.append(lo)
+            done = torch.cuda.Event()
+            done.record(sa)
+            sb.wait_event(done)  # layer l's write after its last attention call, beside layer l+1's
+            views[l].write_chunk(clean[l][0], clean[l][1], stream=sb)
+        committed = torch.cuda.Event()
+        committed.record(sb)
+        assert cache.append_commit() == model.append()
+        keep.append((dev, clean))
+        results.append((xs, outs))
+    torch.cuda.synchronize()
+    hist = [({}, {}) for _ in range(L)]
+    for c, (xs, outs) in enumerate(results):
+        for l in range(L):
+            x = xs[l]
+            for s, (o, lse) in enumerate(outs[l]):
+                ref, ref_lse = attend_chunk(c, x.q[s], store(x.k[s]), store(x.v[s]), hist[l][0].__getitem__,
+                                            hist[l][1].__getitem__, store(conds[l][0]), store(conds[l][1]), W, 1,
+                                            specs[l].scale)
+                _check(from_dev(o), lse.cpu().numpy().astype(np.float64), ref, ref_lse, fp8,
+                       "overlap %s chunk %d layer %d step %d" % (kv_dtype, c, l, s))
+            hist[l][0][c], hist[l][1][c] = store(x.k_clean), store(x.v_clean)
+    cache.close()
