@@ -60,8 +60,15 @@ constexpr float kP8Slack = 2.75f;  // lazy-rescale slack of the fp8 kernel (log2
 
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 
-template <int D>
+// Schedules of the key-tile loop (see the kernel).
+constexpr int kF8Lockstep = 0;  // all waves in the same phase; two LDS buffers
+constexpr int kF8PingPong = 1;  // two wave groups in alternate phases; four LDS buffers
+
+template <int D, int SCHED_ = kF8PingPong>
 struct F8Cfg {
+  static constexpr int SCHED = SCHED_;
+  static constexpr bool PP = SCHED == kF8PingPong;
+  static constexpr int NBUF = PP ? 4 : 2;
   static constexpr int NW = 8;
   static constexpr int NT = NW * 64;
   static constexpr int ROWS = NW * 32;   // query rows a unit can hold
@@ -95,11 +102,11 @@ __device__ __forceinline__ unsigned pk4_fp8(float a, float b, float c, float d) 
   return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
-template <int D>
+template <int D, int SCHED>
 __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
-  using C = F8Cfg<D>;
+  using C = F8Cfg<D, SCHED>;
   constexpr int BN = C::BN;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::BUF_B];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NBUF * C::BUF_B];
   __shared__ float s_ks[kMaxSegments], s_lv[kMaxSegments];  // per segment: K scale, log2(V scale / vs_ref)
 
   int unit, t0 = 0, t1 = a.tiles, piece = -1, ru = 0;
@@ -403,6 +410,200 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
       ++sg;
     }
   }
+  if constexpr (C::PP) {
+    // ---- ping-pong schedule (as in the bf16 kernel).  SIMD s holds wave s
+    // (group A) and wave s + 4 (group B); per key tile j every wave runs
+    //   X_j: S(j) = Kc(j) Q^T (hi and lo parts) and O^T += Vc(j-1)^T P8(j-1)^T
+    //        with the row sum of P8(j-1), then the row max of S(j);
+    //   Y_j: the loads of tile j + 2 and the softmax of S(j) -> P8(j).
+    // Group B runs one phase behind group A and a workgroup barrier ends every
+    // phase, so on each SIMD one wave streams MFMAs while the other runs the
+    // exponentials.  Tile j lives in buffer j % 4, loaded during phases 2j-3
+    // and 2j-2 (the Y_{j-2} of the two groups), read in phases 2j .. 2j+3; each
+    // wave waits for its own loads of tile j by the end of phase 2j-1.
+    const int grp = wave >> 2;
+    const int n = uniform(t1 - t0);  // key tiles of this unit or slice, >= 1
+    Cursor lcur = cur;               // the tile whose loads were issued last
+    {
+      const Plan p = make_plan(lcur, 0);
+#pragma unroll
+      for (int j = 0; j < C::LPW; ++j) load_one(p, j);
+    }
+    if (n > 1) {
+      lcur = advance(lcur);
+      const Plan p = make_plan(lcur, 1);
+#pragma unroll
+      for (int j = 0; j < C::LPW; ++j) load_one(p, j);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (grp == 1) __syncthreads();  // group B starts one phase late
+    Cursor ccur = cur;              // tile j
+    f32x16 sacc[2];
+    i32x8 pv;                       // P8 of tile j-1 (Y_{j-1} -> X_j)
+    int pseg = 0;                   // its segment
+    float mx = 0.f;                 // row max of S(j), scaled (X_j -> Y_j)
+    auto rdk = [&](const uint8_t* t, int kk, int kb) -> i32x8 {
+      const uint4 lo = *(const uint4*)(t + kaddr[kk][0] + kb * 32 * D);
+      const uint4 hi = *(const uint4*)(t + kaddr[kk][1] + kb * 32 * D);
+      return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    auto rdv = [&](const uint8_t* t, int db) -> i32x8 {
+      const uint4 lo = *(const uint4*)(t + vaddr[0] + db * 32 * 64);
+      const uint4 hi = *(const uint4*)(t + vaddr[1] + db * 32 * 64);
+      return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    // X: the operands of one 64-deep step are read one step ahead of its four
+    // MFMAs (hi part of both key blocks, then lo), the first V^T operands
+    // during the last S step; sched_barrier keeps that order.
+    auto phase_x = [&](auto do_s, auto do_pv, int j) {
+      constexpr bool DO_S = decltype(do_s)::value, DO_PV = decltype(do_pv)::value;
+      if (!wave_active) return;
+      __builtin_amdgcn_s_setprio(2);
+      const uint8_t* tk = lds + (j & 3) * C::BUF_B;
+      const uint8_t* tv = lds + ((j + 3) & 3) * C::BUF_B;
+      if constexpr (DO_PV) {
+        if (pseg != lseg) {
+          flush_sum();
+          lseg = pseg;
+        }
+      }
+      i32x8 ka[C::KK][2], va[C::DB];
+      if constexpr (DO_S) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+        ka[0][0] = rdk(tk, 0, 0);
+        ka[0][1] = rdk(tk, 0, 1);
+#pragma unroll
+        for (int kk = 0; kk < C::KK; ++kk) {
+          if (kk + 1 < C::KK) {
+            ka[kk + 1][0] = rdk(tk, kk + 1, 0);
+            ka[kk + 1][1] = rdk(tk, kk + 1, 1);
+          } else if constexpr (DO_PV) {
+            va[0] = rdv(tv, 0);
+            va[1] = rdv(tv, 1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int kb = t & 1;
+            if (t < 2)
+              sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[kk][kb], qhi[kk], sacc[kb], 0, 0, 0, 127,
+                                                                         0, 127);
+            else
+              sacc[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[kk][kb], qlo[kk], sacc[kb], 0, 0, 0, 127,
+                                                                         0, 123);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      } else {
+        va[0] = rdv(tv, 0);
+        va[1] = rdv(tv, 1);
+      }
+      if constexpr (DO_PV) {
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          if (db + 2 < C::DB) va[db + 2] = rdv(tv, db + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[db], pv, oacc[db], 0, 0, 0, 127, 0, 127);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pv, lacc, 0, 0, 0, 127, 0, 127);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      if constexpr (DO_S) {
+        const int valid = uniform(min(BN, ccur.len - ccur.off));
+        if (valid < BN) {  // key of register r = kb*32 + 16*hf + r
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (kb * 32 + 16 * hf + r >= valid) sacc[kb][r] = kNegInf;
+        }
+        float mx0 = kNegInf, mx1 = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          mx0 = fmaxf(mx0, sacc[0][r]);
+          mx1 = fmaxf(mx1, sacc[1][r]);
+        }
+        mx = max_halves(fmaxf(mx0, mx1)) * (cq * s_ks[uniform(ccur.seg)]);
+      }
+    };
+    // Y: the loads of tile j + 2, the softmax of S(j) -> P8(j).  Returns
+    // whether loads were issued.
+    auto phase_y = [&](int j) -> bool {
+      __builtin_amdgcn_s_setprio(1);  // above the MFMA wave's row max
+      bool issued = false;
+      if (j + 2 < n) {
+        lcur = advance(lcur);
+        const Plan p = make_plan(lcur, (j + 2) & 3);
+#pragma unroll
+        for (int i = 0; i < C::LPW; ++i) load_one(p, i);
+        issued = true;
+      }
+      if (wave_active) {
+        const int sg = uniform(ccur.seg);
+        const float mult = cq * s_ks[sg];
+        if (__any(mx > m_run + kP8Slack)) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
+        }
+        const float bias = s_lv[sg] - m_run + kP8Offset;
+        unsigned pw[8];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float e0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 0], mult, bias));
+            const float e1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 1], mult, bias));
+            const float e2 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 2], mult, bias));
+            const float e3 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][4 * w + 3], mult, bias));
+            pw[kb * 4 + w] = pk4_fp8(e0, e1, e2, e3);
+          }
+        pv = i32x8{(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3], (int)pw[4], (int)pw[5], (int)pw[6], (int)pw[7]};
+        pseg = sg;
+      }
+      ccur = advance(ccur);
+      __builtin_amdgcn_s_setprio(0);
+      return issued;
+    };
+    // barriers: group A waits for its own loads at the end of its Y phases,
+    // group B at the end of its X phases (both odd global phases)
+    auto end_x = [&]() {
+      if (grp == 1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+    };
+    auto end_y = [&](bool issued) {
+      if (grp == 0) {
+        if (issued)
+          __builtin_amdgcn_s_waitcnt((0x0F70 & ~0xF) | C::LPW);  // all but this phase's loads
+        else
+          __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
+      __syncthreads();
+    };
+    phase_x(std::true_type(), std::false_type(), 0);
+    end_x();
+    for (int j = 1; j < n; ++j) {
+      end_y(phase_y(j - 1));
+      phase_x(std::true_type(), std::true_type(), j);
+      end_x();
+    }
+    end_y(phase_y(n - 1));
+    phase_x(std::false_type(), std::true_type(), n);
+    end_x();
+    if (grp == 0) __syncthreads();  // group A's trailing phase
+  } else {
   int left = uniform(t1 - t0);  // >= 1
   {
     const Plan p0 = make_plan(cur, 0);
@@ -427,6 +628,7 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     cur = nxt;
+  }
   }
 
   flush_sum();
@@ -515,8 +717,13 @@ __global__ __launch_bounds__(64) void merge_slices_kernel(AttnArgs a) {
 
 constexpr int kMaxSlicesF8 = 8;
 
+// launch configurations: the schedule of the key-tile loop (8 waves, one
+// workgroup per CU in both)
+constexpr int kF8Cfg[] = {kF8PingPong, kF8Lockstep};
+constexpr int kF8Configs = sizeof(kF8Cfg) / sizeof(kF8Cfg[0]);
+
 template <int D>
-int launch_fp8(AttnArgs& a, hipStream_t stream) {
+int launch_fp8(AttnArgs& a, int config, hipStream_t stream) {
   using C = F8Cfg<D>;
   a.q_tiles = (a.Tq + C::ROWS - 1) / C::ROWS;
   a.q_rows = (a.Tq + a.q_tiles - 1) / a.q_tiles;  // equal tiles
@@ -548,7 +755,10 @@ int launch_fp8(AttnArgs& a, hipStream_t stream) {
   }
   a.grid_whole = 8 * ((a.n_whole + 7) / 8);
   const int grid = a.grid_whole + 8 * ((a.rest * a.slices + 7) / 8);
-  hipLaunchKernelGGL((attention_fp8_kernel<D>), dim3(grid), dim3(C::NT), 0, stream, a);
+  if (kF8Cfg[config] == kF8PingPong)
+    hipLaunchKernelGGL((attention_fp8_kernel<D, kF8PingPong>), dim3(grid), dim3(C::NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attention_fp8_kernel<D, kF8Lockstep>), dim3(grid), dim3(C::NT), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return -1;
   if (a.slices > 1) {
     hipLaunchKernelGGL((merge_slices_kernel<D>), dim3(a.rest * C::NW), dim3(64), 0, stream, a);
@@ -559,9 +769,19 @@ int launch_fp8(AttnArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-int launch_attention_fp8(AttnArgs& a, int head_dim, hipStream_t stream) {
-  if (head_dim == 128) return launch_fp8<128>(a, stream);
-  if (head_dim == 64) return launch_fp8<64>(a, stream);
+int attention_fp8_configs(int* waves, int* wgs, int* sched, int cap) {
+  for (int i = 0; i < kF8Configs && i < cap; ++i) {
+    if (waves) waves[i] = F8Cfg<128>::NW;
+    if (wgs) wgs[i] = 1;
+    if (sched) sched[i] = kF8Cfg[i];
+  }
+  return kF8Configs;
+}
+
+int launch_attention_fp8(AttnArgs& a, int head_dim, int config, hipStream_t stream) {
+  if (config < 0 || config >= kF8Configs) return -2;
+  if (head_dim == 128) return launch_fp8<128>(a, config, stream);
+  if (head_dim == 64) return launch_fp8<64>(a, config, stream);
   return -2;
 }
 

@@ -277,7 +277,7 @@ int attention_call(kvc_cache* h, int n_q, const void* q, const void* k_cur, cons
       rc = quantize_into(h, k_cur, v_cur, h->T, cur_row0, n_slots + 1, kSiteAttention, st);
     }
     if (rc != 0) return fail(KVC_ERR_HIP, "%s: quantise launch failed", who);
-    if (kvc::launch_attention_fp8(a, h->D, st) != 0) return fail(KVC_ERR_HIP, "%s: launch failed", who);
+    if (kvc::launch_attention_fp8(a, h->D, h->config, st) != 0) return fail(KVC_ERR_HIP, "%s: launch failed", who);
     return KVC_OK;
   }
   const std::vector<kvc::Segment> segs = h->tbl().segments(h->T, h->Lc, true, h->cond_rows());
@@ -584,7 +584,8 @@ int sink_window_attention_noalloc(kvc_handle h, const void* q, const void* k_cur
 }
 
 static int config_count(const kvc_cache* h) {
-  return h->kv_dtype == KVC_KV_FP8 ? 1 : kvc::attention_bf16_configs(h->D, nullptr, nullptr, nullptr, 0);
+  return h->kv_dtype == KVC_KV_FP8 ? kvc::attention_fp8_configs(nullptr, nullptr, nullptr, 0)
+                                   : kvc::attention_bf16_configs(h->D, nullptr, nullptr, nullptr, 0);
 }
 
 int kv_cache_config_count(kvc_handle h, int* out_count) {
@@ -599,15 +600,13 @@ int kv_cache_config_info(kvc_handle h, int id, int* waves_per_workgroup, int* wo
   if (!h) return fail(KVC_ERR_INVALID, "kv_cache_config_info: handle is NULL");
   const int n = config_count(h);
   if (id < 0 || id >= n) return fail(KVC_ERR_INVALID, "kv_cache_config_info: config %d outside [0, %d)", id, n);
-  int w = 8, g = 1;  // fp8: its one configuration
-  if (h->kv_dtype != KVC_KV_FP8) {
-    int ws[16], gs[16];
+  int ws[16], gs[16];
+  if (h->kv_dtype == KVC_KV_FP8)
+    kvc::attention_fp8_configs(ws, gs, nullptr, 16);
+  else
     kvc::attention_bf16_configs(h->D, ws, gs, nullptr, 16);
-    w = ws[id];
-    g = gs[id];
-  }
-  if (waves_per_workgroup) *waves_per_workgroup = w;
-  if (workgroups_per_cu) *workgroups_per_cu = g;
+  if (waves_per_workgroup) *waves_per_workgroup = ws[id];
+  if (workgroups_per_cu) *workgroups_per_cu = gs[id];
   return KVC_OK;
 }
 

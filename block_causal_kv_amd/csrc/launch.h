@@ -113,8 +113,11 @@ int launch_fill_spans(void* base, int64_t n_spans, int64_t stride, int64_t off, 
 // (looked up once per device); bytes receives its size.  Returns 0 or -1.
 int static_scratch(void** ptr, size_t* bytes);
 
-// fp8 attention (E4M3 K/V codes, per-(head, chunk) scales).
-int launch_attention_fp8(AttnArgs& a, int head_dim, hipStream_t stream);
+// fp8 attention (E4M3 K/V codes, per-(head, chunk) scales).  config indexes
+// the launch configurations that attention_fp8_configs lists (waves per
+// workgroup, workgroups per CU, schedule: 1 ping-pong, 0 lockstep).
+int attention_fp8_configs(int* waves, int* wgs, int* sched, int cap);
+int launch_attention_fp8(AttnArgs& a, int head_dim, int config, hipStream_t stream);
 
 // Quantise K and V (bf16 [H][rows][D]) into E4M3 codes: K row-major into
 // k_dst[h*k_head + (row0 + r)*D + d], V transposed into vt_dst[(h*D + d)*vt_rows + row0 + r];

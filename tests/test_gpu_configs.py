@@ -1,6 +1,7 @@
 """Every launch configuration of the bf16 attention kernel (waves per
-workgroup x workgroups per CU) against the oracle, and the measured choice
-among them (kv_cache_autotune).  Tolerances as for one cache call."""
+workgroup x workgroups per CU x schedule) and of the fp8 kernel (schedule)
+against the oracle, and the measured choice among them (kv_cache_autotune).
+Tolerances as for one cache call."""
 import numpy as np
 import pytest
 
@@ -31,6 +32,30 @@ def test_config_many_units(D, cfg):
     spec = synthetic.small_spec("cfg_big", n_chunks=4, chunk_tokens=1100, cond_len=64, heads=96, head_dim=D,
                                 window=2, seed=50 + cfg)
     rows = np.array(sorted(set(range(0, 1100, 37)) | set(range(1090, 1100))))
+    run_stream(spec, [0, 3], rows=rows, config=cfg)
+
+
+# fp8: configuration 0 is the ping-pong schedule, 1 the lockstep one
+F8_CASES = [(D, c) for D in (128, 64) for c in range(2)]
+
+
+@pytest.mark.parametrize("D,cfg", F8_CASES, ids=["fp8-d%d-c%d" % c for c in F8_CASES])
+def test_fp8_config_parity(D, cfg):
+    # several query tiles with a ragged last one, two steps, outlier keys
+    spec = synthetic.small_spec("cfg8", n_chunks=5, chunk_tokens=304, cond_len=32, heads=5, head_dim=D,
+                                window=2, steps=2, clean_from_last_step=False, outlier_frac=0.01, seed=70 + cfg,
+                                kv_dtype="fp8")
+    say("fp8 config %d, D=%d" % (cfg, D))
+    run_stream(spec, range(spec.n_chunks), config=cfg)
+
+
+@pytest.mark.parametrize("D,cfg", F8_CASES, ids=["fp8-d%d-c%d" % c for c in F8_CASES])
+def test_fp8_config_many_units(D, cfg):
+    """Units over more than one round of workgroup slots: the key-slice split
+    and its merge run with each schedule."""
+    spec = synthetic.small_spec("cfg8_big", n_chunks=4, chunk_tokens=1104, cond_len=64, heads=96, head_dim=D,
+                                window=2, seed=75 + cfg, kv_dtype="fp8")
+    rows = np.array(sorted(set(range(0, 1104, 37)) | set(range(1094, 1104))))
     run_stream(spec, [0, 3], rows=rows, config=cfg)
 
 
@@ -84,7 +109,9 @@ def test_config_table_and_autotune():
         assert (o - outs[0]).abs().max().item() < 2e-2
     cache.close()
     f8 = KVCache(64, 2, 1, 16, 2, 128, "fp8")
-    assert f8.configs() == [(8, 1)]
+    assert f8.configs() == [(8, 1), (8, 1)]
+    with pytest.raises(KVCError):
+        f8.config = 2
     f8.close()
 
 
