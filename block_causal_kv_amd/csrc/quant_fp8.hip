@@ -12,7 +12,8 @@
 // [H][D][rows] (the PV product reads V^T, and the transposition is free here).
 // Two kernels: a per-head absolute maximum (atomic max on the float's bits,
 // which order like the values for non-negative floats), then the quantising
-// write, which also records the scale.  The maxima live in one of two
+// write, which also records the scale (the second pass over the input mostly
+// hits the cache: a chunk's K and V are tens of MB).  The maxima live in one of two
 // buffers used in turn; each quantisation clears the other one for the next.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -22,44 +23,48 @@
 namespace kvc {
 namespace {
 
-// Round-to-nearest-even E4M3 code of a finite float, saturating at +-448.
-// Bit layout: sign 1, exponent 4 (bias 7), mantissa 3; exponent field 0 holds
-// the subnormals m * 2^-9.
-__device__ __forceinline__ uint32_t e4m3_rne(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = fabsf(y);
-  uint32_t mag;
-  if (!(a <= 448.0f)) {
-    mag = 0x7Eu;  // saturate
-  } else if (a < 0.015625f) {  // below 2^-6: subnormal grid of step 2^-9 (exact scaling)
-    mag = (uint32_t)__builtin_rintf(a * 512.0f);  // 0..8; 8 is the smallest normal (code 0x08)
-  } else {
-    const uint32_t ua = __float_as_uint(a);
-    int e = (int)((ua >> 23) & 0xFF) - 127;  // -6 .. 8
-    uint32_t m = (ua >> 20) & 7u;            // top 3 mantissa bits
-    const uint32_t rest = ua & 0xFFFFFu;     // the 20 bits below them
-    if (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) ++m;
-    if (m == 8u) {
-      m = 0;
-      ++e;
-    }
-    mag = (e > 8 || (e == 8 && m == 7u)) ? 0x7Eu : (uint32_t)((e + 7) << 3) | m;
+// x / scale rounded to nearest float32, for one scale shared by many x:
+// q0 = x * (1/scale) is within an ulp of the quotient, the residual
+// x - q0 * scale is exact by FMA, and one FMA step with the correctly rounded
+// reciprocal gives the correctly rounded quotient (Markstein's theorem on
+// division by FMA; it needs no underflow, so scales below 2^-64 take the
+// plain division instead).  The quotient takes the sign of x: for x = -0 the
+// residual step would return +0.
+struct Divider {
+  float scale, inv;
+  bool tiny;
+  __device__ explicit Divider(float s) : scale(s), inv(1.0f / s), tiny(s < 0x1p-64f) {}
+  __device__ __forceinline__ float operator()(float x) const {
+    if (tiny) return x / scale;
+    const float q0 = x * inv;
+    const float r = fmaf(-q0, scale, x);
+    return copysignf(fmaf(r, inv, q0), x);
   }
-  return sign | mag;
+};
+
+// Four floats -> four E4M3 codes in one dword (round to nearest even; the
+// converter's own rounding).  Every quotient here is at most 448 (1 + 2^-23)
+// in magnitude, below the first value that rounds past 448.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
-// amax of K (tensor 0) and V (tensor 1) per head: grid (blocks, H, 2).
+// amax of K (tensor 0) and V (tensor 1) per head: grid (blocks, H, 2), each
+// thread four independent 16-byte loads.
+constexpr int kAmaxLoads = 4;
 __global__ __launch_bounds__(256) void amax_bf16_kernel(const uint16_t* __restrict__ k,
-                                                        const uint16_t* __restrict__ v, int64_t per_head,
+                                                        const uint16_t* __restrict__ v, int n16,
                                                         uint32_t* __restrict__ amax_bits) {
-  const uint16_t* src = (blockIdx.z == 0 ? k : v) + (int64_t)blockIdx.y * per_head;
+  const uint4* src = (const uint4*)((blockIdx.z == 0 ? k : v) + (int64_t)blockIdx.y * n16 * 8);
+  const int i0 = blockIdx.x * (256 * kAmaxLoads) + threadIdx.x;
+  uint4 w[kAmaxLoads];
+#pragma unroll
+  for (int u = 0; u < kAmaxLoads; ++u) w[u] = i0 + 256 * u < n16 ? src[i0 + 256 * u] : make_uint4(0, 0, 0, 0);
   float m = 0.f;
-#pragma unroll 4
-  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8; i < per_head;
-       i += (int64_t)gridDim.x * blockDim.x * 8) {
-    const uint4 w = *(const uint4*)(src + i);  // per_head is a multiple of 8 (D in {64, 128})
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int u = 0; u < kAmaxLoads; ++u) {
+    const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       m = fmaxf(m, fabsf(__uint_as_float(ws[j] << 16)));
@@ -76,63 +81,92 @@ __global__ __launch_bounds__(256) void amax_bf16_kernel(const uint16_t* __restri
   }
 }
 
-// Quantise 64 rows of K and V for one head (grid: row tiles, H, 2):
-// K codes -> k_dst[h*k_head + (row0 + r)*D + d], V codes -> vt_dst[(h*D + d)*vt_rows + row0 + r].
-// scales[tensor * scale_tensor + h * scale_head] <- scale.
+// Quantise 64 rows of K or V for one head (grid: row tiles, H, 2 tensors;
+// D/8 x 16 threads): K codes -> k_dst[h*k_head + (row0 + r)*D + d], V codes ->
+// vt_dst[(h*D + d)*vt_rows + row0 + r]; scales[tensor * scale_tensor + h *
+// scale_head] <- scale.  Thread (rg, c) takes rows 4rg .. 4rg+3 of the tile
+// and dims 8c .. 8c+7.  V: each 4 x 4 byte block is transposed in registers
+// (byte permutes), staged as [D][64] bytes in LDS (16-byte granules XOR-swizzled
+// by dim) and written as 16-byte pieces of V^T rows.
 template <int D>
-__global__ __launch_bounds__(256) void quantize_bf16_kernel(const uint16_t* __restrict__ k,
-                                                            const uint16_t* __restrict__ v, int rows,
-                                                            const uint32_t* __restrict__ amax_bits,
-                                                            uint8_t* __restrict__ k_dst, int64_t k_head,
-                                                            uint8_t* __restrict__ vt_dst, int64_t vt_rows,
-                                                            int row0, float* __restrict__ scales,
-                                                            int scale_tensor, int scale_head,
-                                                            uint32_t* __restrict__ amax_next, int n_next) {
-  constexpr int TR = 64;  // rows per block
+__global__ __launch_bounds__(D * 2) void quantize_bf16_kernel(const uint16_t* __restrict__ k,
+                                                              const uint16_t* __restrict__ v, int rows,
+                                                              const uint32_t* __restrict__ amax_bits,
+                                                              uint8_t* __restrict__ k_dst, int64_t k_head,
+                                                              uint8_t* __restrict__ vt_dst, int64_t vt_rows,
+                                                              int row0, float* __restrict__ scales,
+                                                              int scale_tensor, int scale_head,
+                                                              uint32_t* __restrict__ amax_next, int n_next) {
+  constexpr int TR = 64;     // rows per block
+  constexpr int NC = D / 8;  // 8-dim pieces per row
+  constexpr int NT = NC * (TR / 4);
   // the other amax buffer, used by the next quantisation, starts at zero
   if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
-    for (int i = threadIdx.x; i < n_next; i += blockDim.x) amax_next[i] = 0u;
-  __shared__ uint8_t tile[D][TR + 16];
+    for (int i = threadIdx.x; i < n_next; i += NT) amax_next[i] = 0u;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[D * TR];
   const int tensor = blockIdx.z;
   const int h = blockIdx.y;
   const int r0 = blockIdx.x * TR;
+  const int nr = min(TR, rows - r0);  // rows of this tile
   const float amax = __uint_as_float(amax_bits[tensor * gridDim.y + h]);
   const float scale = amax > 0.f ? amax / 448.0f : 1.0f;  // correctly rounded float32 division
   if (blockIdx.x == 0 && threadIdx.x == 0) scales[tensor * scale_tensor + h * scale_head] = scale;
-  const uint16_t* src = (tensor == 0 ? k : v) + ((int64_t)h * rows + r0) * D;
-  constexpr int CH = D / 8;  // 8-element pieces per row
-  for (int idx = threadIdx.x; idx < TR * CH; idx += blockDim.x) {
-    const int r = idx / CH, c8 = idx % CH;
-    if (r0 + r >= rows) continue;
-    const uint4 w = *(const uint4*)(src + (int64_t)r * D + c8 * 8);
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-    uint32_t codes[8];
+  const Divider div(scale);
+  const int c = threadIdx.x % NC, rg = threadIdx.x / NC;
+  const uint16_t* src = (tensor == 0 ? k : v) + ((int64_t)h * rows + r0 + 4 * rg) * D + 8 * c;
+  uint4 w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = 4 * rg + i < nr ? *(const uint4*)(src + i * D) : make_uint4(0, 0, 0, 0);
+  uint32_t lo[4], hi[4];  // row i: codes of dims 8c .. 8c+3 (lo) and 8c+4 .. 8c+7 (hi)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t ws[4] = {w[i].x, w[i].y, w[i].z, w[i].w};
+    float f[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      codes[2 * j] = e4m3_rne(__uint_as_float(ws[j] << 16) / scale);
-      codes[2 * j + 1] = e4m3_rne(__uint_as_float(ws[j] & 0xFFFF0000u) / scale);
+      f[2 * j] = div(__uint_as_float(ws[j] << 16));
+      f[2 * j + 1] = div(__uint_as_float(ws[j] & 0xFFFF0000u));
     }
-    if (tensor == 0) {
-      const uint2 packed = make_uint2(codes[0] | (codes[1] << 8) | (codes[2] << 16) | (codes[3] << 24),
-                                      codes[4] | (codes[5] << 8) | (codes[6] << 16) | (codes[7] << 24));
-      *(uint2*)(k_dst + (int64_t)h * k_head + (int64_t)(row0 + r0 + r) * D + c8 * 8) = packed;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) tile[c8 * 8 + j][r] = (uint8_t)codes[j];
-    }
+    lo[i] = e4m3x4(f[0], f[1], f[2], f[3]);
+    hi[i] = e4m3x4(f[4], f[5], f[6], f[7]);
   }
-  if (tensor == 0) return;
+  if (tensor == 0) {
+    uint8_t* dst = k_dst + (int64_t)h * k_head + (int64_t)(row0 + r0 + 4 * rg) * D + 8 * c;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * rg + i < nr) *(uint2*)(dst + (int64_t)i * D) = make_uint2(lo[i], hi[i]);
+    return;
+  }
+  // 4 x 4 byte transposes: column d of rows 0..3 -> one dword (row 0 in the low byte)
+  uint32_t col[8];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const uint32_t* R = half == 0 ? lo : hi;
+    const uint32_t t0 = __builtin_amdgcn_perm(R[1], R[0], 0x06020400u);  // r0.b0 r1.b0 r0.b2 r1.b2
+    const uint32_t t1 = __builtin_amdgcn_perm(R[1], R[0], 0x07030501u);  // r0.b1 r1.b1 r0.b3 r1.b3
+    const uint32_t t2 = __builtin_amdgcn_perm(R[3], R[2], 0x06020400u);
+    const uint32_t t3 = __builtin_amdgcn_perm(R[3], R[2], 0x07030501u);
+    col[4 * half + 0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+    col[4 * half + 1] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+    col[4 * half + 2] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+    col[4 * half + 3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+  }
+  // LDS: row d holds 64 bytes = granules g of 16 bytes at (g ^ (d >> 3 & 3))
+  auto lds_off = [](int d, int byte) { return d * TR + ((((byte >> 4) ^ (d >> 3)) & 3) << 4) + (byte & 15); };
+#pragma unroll
+  for (int j = 0; j < 8; ++j) *(uint32_t*)(tile + lds_off(8 * c + j, 4 * rg)) = col[j];
   __syncthreads();
-  // V^T rows: D rows of up to 64 codes, written 4 bytes at a time
-  const int nr = min(TR, rows - r0);
-  for (int idx = threadIdx.x; idx < D * (TR / 4); idx += blockDim.x) {
-    const int d = idx / (TR / 4), q = idx % (TR / 4);
-    if (4 * q >= nr) continue;
-    uint8_t* dst = vt_dst + ((int64_t)h * D + d) * vt_rows + row0 + r0 + 4 * q;
-    if (4 * q + 4 <= nr && ((row0 + r0) & 3) == 0 && (vt_rows & 3) == 0) {
-      *(uint32_t*)dst = *(const uint32_t*)&tile[d][4 * q];
+  // V^T rows: D rows of nr codes, 16 bytes per thread and step
+  const bool aligned = ((row0 + r0) & 15) == 0 && (vt_rows & 15) == 0;
+  for (int idx = threadIdx.x; idx < D * (TR / 16); idx += NT) {
+    const int d = idx / (TR / 16), g = idx % (TR / 16);
+    if (16 * g >= nr) continue;
+    uint8_t* dst = vt_dst + ((int64_t)h * D + d) * vt_rows + row0 + r0 + 16 * g;
+    const uint8_t* s = tile + lds_off(d, 16 * g);
+    if (aligned && 16 * g + 16 <= nr) {
+      *(uint4*)dst = *(const uint4*)s;
     } else {
-      for (int j = 0; j < 4 && 4 * q + j < nr; ++j) dst[j] = tile[d][4 * q + j];
+      for (int j = 0; j < 16 && 16 * g + j < nr; ++j) dst[j] = s[j];
     }
   }
 }
@@ -144,16 +178,15 @@ int launch_quantize_fp8(const uint16_t* k, const uint16_t* v, int H, int rows, i
                         int64_t vt_rows, int row0, float* scales, int scale_tensor, int scale_head,
                         hipStream_t stream) {
   if (rows <= 0) return 0;
-  const int64_t per_head = (int64_t)rows * D;
-  int blocks = (int)((per_head / 8 + 255) / 256);
-  if (blocks > 64) blocks = 64;
-  hipLaunchKernelGGL(amax_bf16_kernel, dim3(blocks, H, 2), dim3(256), 0, stream, k, v, per_head, amax_bits);
+  const int n16 = rows * D / 8;  // 16-byte pieces per head (D in {64, 128})
+  const int blocks = (n16 + 256 * kAmaxLoads - 1) / (256 * kAmaxLoads);
+  hipLaunchKernelGGL(amax_bf16_kernel, dim3(blocks, H, 2), dim3(256), 0, stream, k, v, n16, amax_bits);
   const dim3 grid((rows + 63) / 64, H, 2);
   if (D == 128)
     hipLaunchKernelGGL(quantize_bf16_kernel<128>, grid, dim3(256), 0, stream, k, v, rows, amax_bits, k_dst,
                        k_head, vt_dst, vt_rows, row0, scales, scale_tensor, scale_head, amax_next, n_amax);
   else if (D == 64)
-    hipLaunchKernelGGL(quantize_bf16_kernel<64>, grid, dim3(256), 0, stream, k, v, rows, amax_bits, k_dst,
+    hipLaunchKernelGGL(quantize_bf16_kernel<64>, grid, dim3(128), 0, stream, k, v, rows, amax_bits, k_dst,
                        k_head, vt_dst, vt_rows, row0, scales, scale_tensor, scale_head, amax_next, n_amax);
   else
     return -2;

@@ -79,7 +79,8 @@ def test_fp8_codes_and_scales_bit_exact(name):
 
 def test_fp8_rounding_ties():
     """Every E4M3 midpoint, with amax = 448 exactly so that scale = 1 and
-    x / scale = x: each tie must round to the even code."""
+    x / scale = x: each tie must round to the even code.  V = -x also holds
+    negative zeros, whose code is 0x80."""
     import torch
     from block_causal_kv_amd import KVCache
     codes = np.arange(0x7E)
@@ -97,6 +98,7 @@ def test_fp8_rounding_ties():
     kc, vt, scales = _pool(cache)
     assert scales[0, 0, 1] == 1.0 and scales[1, 0, 1] == 1.0
     _check_block(kc, vt, scales, x, -x, 0, 1)
+    assert (vt[0, :, :T].T[x[0] == 0] == 0x80).all()
     cache.close()
 
 
