@@ -233,8 +233,8 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
     const int has_cond = STREAM ? (a.cond_len > 0 ? 1 : 0) : 0;
     if constexpr (STREAM)
       t1 = has_cond * ((a.cond_len + C::BN - 1) / C::BN) + (ns + chunk - lo + 1) * ((a.T + C::BN - 1) / C::BN);
-    const int head = unit / a.q_tiles;
-    const int qtile = unit % a.q_tiles;
+    const int head = unit_of(a, unit) / a.q_tiles;
+    const int qtile = unit_of(a, unit) % a.q_tiles;
 
     // first row of this head's queries (stream form: of this chunk's queries)
     const int Tq = STREAM ? T : a.Tq;
@@ -992,7 +992,7 @@ __global__ __launch_bounds__(64) void merge_pieces_kernel(AttnArgs a) {
   const int r_first = range_of(u0, a.total, a.n_ranges);
   const int r_last = range_of(u0 + a.tiles - 1, a.total, a.n_ranges);
   if (r_first == r_last) return;  // the unit was computed whole
-  const int head = unit / a.q_tiles, qtile = unit % a.q_tiles;
+  const int head = unit_of(a, unit) / a.q_tiles, qtile = unit_of(a, unit) % a.q_tiles;
   const int row_beg = qtile * a.q_rows;
   const int row_end = min(a.Tq, row_beg + a.q_rows);
   if (row_beg + wave * 32 >= row_end) return;  // (wave-uniform) no rows
@@ -1094,6 +1094,8 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
   a.total = (int64_t)rest * tiles;
   a.n_ranges = n_ranges;
   a.grid_whole = 8 * ((a.n_whole + 7) / 8);
+  // XCD grouping when both blocks of the schedule divide evenly over the XCDs
+  a.xcd_units = units % 8 == 0 && a.n_whole % 8 == 0 && n_ranges % 8 == 0 ? units / 8 : 0;
   const int grid = a.grid_whole + 8 * ((a.n_ranges + 7) / 8);
   hipLaunchKernelGGL((attention_bf16_kernel<D, NW, WGS, SCHED, false>), dim3(grid), dim3(C::NT), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return -1;
@@ -1112,6 +1114,7 @@ int launch_chunks(AttnArgs& a, hipStream_t stream) {
   a.q_tiles = (a.T + C::ROWS - 1) / C::ROWS;
   a.q_rows = (a.T + a.q_tiles - 1) / a.q_tiles;  // equal tiles
   const int grid = a.H * a.n_chunks * a.q_tiles;
+  a.xcd_units = 0;
   hipLaunchKernelGGL((attention_bf16_kernel<D, NW, WGS, SCHED, true>), dim3(grid), dim3(C::NT), 0, stream, a);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 namespace kvc {
 namespace dev {
 
@@ -62,6 +64,19 @@ struct Cursor {
 };
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Actual unit (head * q_tiles + query tile) of schedule unit s.  Workgroups
+// of XCD x take the whole schedule units [x, x + 1) * n_whole / 8 and the
+// split schedule units [x, x + 1) * rest / 8; with xcd_units > 0 both blocks
+// map into the actual units [x, x + 1) * xcd_units.
+__device__ __forceinline__ int unit_of(const AttnArgs& a, int s) {
+  if (a.xcd_units == 0) return s;
+  const int wpx = a.n_whole / 8;  // whole units per XCD
+  if (s < a.n_whole) return (s / wpx) * a.xcd_units + s % wpx;
+  const int spx = a.xcd_units - wpx;  // split units per XCD
+  const int t = s - a.n_whole;
+  return (t / spx) * a.xcd_units + wpx + t % spx;
+}
 
 // Scheduling pattern for a block of N LDS operand reads feeding N MFMAs: issue
 // 4 reads first, then alternate MFMA / read, so about 4 reads are in flight

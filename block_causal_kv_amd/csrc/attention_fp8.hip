@@ -122,17 +122,26 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
       const int n_pieces = a.rest * a.slices;
       const int per_xcd = (n_pieces + 7) / 8;
       const int k_in = (b - a.grid_whole) / 8;
-      piece = xcd * per_xcd + k_in;
-      if (k_in >= per_xcd || piece >= n_pieces) return;
-      const int slice = piece / a.rest;
-      ru = piece % a.rest;
+      int slice;
+      if (a.xcd_units > 0) {  // XCD x: every slice of the split units [x, x + 1) * rest / 8
+        const int rpx = a.rest / 8;
+        if (k_in >= per_xcd) return;
+        slice = k_in / rpx;
+        ru = xcd * rpx + k_in % rpx;
+        piece = slice * a.rest + ru;
+      } else {
+        piece = xcd * per_xcd + k_in;
+        if (k_in >= per_xcd || piece >= n_pieces) return;
+        slice = piece / a.rest;
+        ru = piece % a.rest;
+      }
       unit = a.n_whole + ru;
       t0 = (int)((int64_t)slice * a.tiles / a.slices);
       t1 = (int)((int64_t)(slice + 1) * a.tiles / a.slices);
     }
   }
-  const int head = unit / a.q_tiles;
-  const int qtile = unit % a.q_tiles;
+  const int head = unit_of(a, unit) / a.q_tiles;
+  const int qtile = unit_of(a, unit) % a.q_tiles;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -677,7 +686,7 @@ __global__ __launch_bounds__(64) void merge_slices_kernel(AttnArgs a) {
   const int unit = a.n_whole + ru;
   const int wave = (int)(blockIdx.x % C::NW), lane = threadIdx.x;
   const int hf = lane >> 5, col = lane & 31;
-  const int head = unit / a.q_tiles, qtile = unit % a.q_tiles;
+  const int head = unit_of(a, unit) / a.q_tiles, qtile = unit_of(a, unit) % a.q_tiles;
   const int row_beg = qtile * a.q_rows;
   const int row_end = min(a.Tq, row_beg + a.q_rows);
   if (row_beg + wave * 32 >= row_end) return;  // (wave-uniform) no rows
@@ -754,6 +763,8 @@ int launch_fp8(AttnArgs& a, int config, hipStream_t stream) {
     a.n_whole = units;
   }
   a.grid_whole = 8 * ((a.n_whole + 7) / 8);
+  // XCD grouping when the whole and the split units divide evenly over the XCDs
+  a.xcd_units = units % 8 == 0 && a.n_whole % 8 == 0 ? units / 8 : 0;
   const int grid = a.grid_whole + 8 * ((a.rest * a.slices + 7) / 8);
   if (kF8Cfg[config] == kF8PingPong)
     hipLaunchKernelGGL((attention_fp8_kernel<D, kF8PingPong>), dim3(grid), dim3(C::NT), 0, stream, a);

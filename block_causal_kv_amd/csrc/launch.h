@@ -53,6 +53,12 @@ struct AttnArgs {
   int grid_whole;
   int n_ranges;
   int64_t total;
+  // XCD grouping (0 = off): the schedule above runs over "schedule units";
+  // with xcd_units > 0 the whole units and the split units that land on XCD
+  // x are the actual units [x * xcd_units, (x + 1) * xcd_units), so every
+  // XCD serves units / 8 consecutive units (H / 8 heads when H is a multiple
+  // of 8) and a head's K/V is fetched into one XCD's L2 only.
+  int xcd_units;
   float* ws_o;     // partial O^T of the slices: [piece][wave][register][lane]
   float* ws_ml;    // partial (max, sum): [piece][wave][2][lane]
   int num_cus;
