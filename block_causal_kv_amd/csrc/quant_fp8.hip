@@ -16,6 +16,8 @@
 // hits the cache: a chunk's K and V are tens of MB).  The maxima live in one of two
 // buffers used in turn; each quantisation clears the other one for the next.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "launch.h"
@@ -50,25 +52,30 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
-// amax of K (tensor 0) and V (tensor 1) per head: grid (blocks, H, 2), each
-// thread four independent 16-byte loads.
-constexpr int kAmaxLoads = 4;
+// amax of K (tensor 0) and V (tensor 1) per head: grid (blocks, H, 2) with
+// at most kAmaxBlocks blocks per (head, tensor), each thread kAmaxLoads
+// independent 16-byte loads per step.  Atomics on one address serialise
+// (about a quarter of a microsecond each on this device), so a (head, tensor)
+// gets few, large blocks rather than many small ones.
+constexpr int kAmaxLoads = 16;
+constexpr int kAmaxBlocks = 16;
 __global__ __launch_bounds__(256) void amax_bf16_kernel(const uint16_t* __restrict__ k,
                                                         const uint16_t* __restrict__ v, int n16,
                                                         uint32_t* __restrict__ amax_bits) {
   const uint4* src = (const uint4*)((blockIdx.z == 0 ? k : v) + (int64_t)blockIdx.y * n16 * 8);
-  const int i0 = blockIdx.x * (256 * kAmaxLoads) + threadIdx.x;
-  uint4 w[kAmaxLoads];
-#pragma unroll
-  for (int u = 0; u < kAmaxLoads; ++u) w[u] = i0 + 256 * u < n16 ? src[i0 + 256 * u] : make_uint4(0, 0, 0, 0);
   float m = 0.f;
+  for (int i0 = blockIdx.x * (256 * kAmaxLoads) + threadIdx.x; i0 < n16; i0 += gridDim.x * (256 * kAmaxLoads)) {
+    uint4 w[kAmaxLoads];
 #pragma unroll
-  for (int u = 0; u < kAmaxLoads; ++u) {
-    const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+    for (int u = 0; u < kAmaxLoads; ++u) w[u] = i0 + 256 * u < n16 ? src[i0 + 256 * u] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      m = fmaxf(m, fabsf(__uint_as_float(ws[j] << 16)));
-      m = fmaxf(m, fabsf(__uint_as_float(ws[j] & 0xFFFF0000u)));
+    for (int u = 0; u < kAmaxLoads; ++u) {
+      const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        m = fmaxf(m, fabsf(__uint_as_float(ws[j] << 16)));
+        m = fmaxf(m, fabsf(__uint_as_float(ws[j] & 0xFFFF0000u)));
+      }
     }
   }
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -179,7 +186,7 @@ int launch_quantize_fp8(const uint16_t* k, const uint16_t* v, int H, int rows, i
                         hipStream_t stream) {
   if (rows <= 0) return 0;
   const int n16 = rows * D / 8;  // 16-byte pieces per head (D in {64, 128})
-  const int blocks = (n16 + 256 * kAmaxLoads - 1) / (256 * kAmaxLoads);
+  const int blocks = std::min((n16 + 256 * kAmaxLoads - 1) / (256 * kAmaxLoads), kAmaxBlocks);
   hipLaunchKernelGGL(amax_bf16_kernel, dim3(blocks, H, 2), dim3(256), 0, stream, k, v, n16, amax_bits);
   const dim3 grid((rows + 63) / 64, H, 2);
   if (D == 128)
