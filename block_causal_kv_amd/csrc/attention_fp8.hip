@@ -691,21 +691,25 @@ __global__ __launch_bounds__(64) void merge_slices_kernel(AttnArgs a) {
   const int row_end = min(a.Tq, row_beg + a.q_rows);
   if (row_beg + wave * 32 >= row_end) return;  // (wave-uniform) no rows
   const int qrow = row_beg + wave * 32 + col;
+  // the final max and sum first, then each slice's partial O^T with one
+  // weight: the loads of a slice do not wait on a running rescale, so all of
+  // them are in flight at once
+  auto slice = [&](int j) { return (size_t)(j * a.rest + ru) * C::NW + wave; };
+  float m = kNegInf, l = 0.f;
+  for (int j = 0; j < a.slices; ++j) m = fmaxf(m, a.ws_ml[slice(j) * 2 * 64 + lane]);
   float o[NR];
 #pragma unroll
   for (int k = 0; k < NR; ++k) o[k] = 0.f;
-  float m = kNegInf, l = 0.f;
   for (int j = 0; j < a.slices; ++j) {
-    const size_t pj = (size_t)(j * a.rest + ru) * C::NW + wave;
-    const float* qo = a.ws_o + pj * NR * 64 + lane;
-    const float* qml = a.ws_ml + pj * 2 * 64 + lane;
-    const float mj = qml[0], lj = qml[64];
-    const float mm = fmaxf(m, mj);
-    const float a0 = __builtin_amdgcn_exp2f(m - mm), a1 = __builtin_amdgcn_exp2f(mj - mm);
+    const float* qo = a.ws_o + slice(j) * NR * 64 + lane;
+    const float* qml = a.ws_ml + slice(j) * 2 * 64 + lane;
+    float t[NR];
 #pragma unroll
-    for (int k = 0; k < NR; ++k) o[k] = o[k] * a0 + qo[k * 64] * a1;
-    l = l * a0 + lj * a1;
-    m = mm;
+    for (int k = 0; k < NR; ++k) t[k] = qo[k * 64];
+    const float w = __builtin_amdgcn_exp2f(qml[0] - m);
+    l += qml[64] * w;
+#pragma unroll
+    for (int k = 0; k < NR; ++k) o[k] = fmaf(t[k], w, o[k]);
   }
   const float l_tot = sum_halves(l);
   if (qrow >= row_end) return;
