@@ -15,6 +15,7 @@ oracle on a bounded sample of the same call.
     python bench.py --chunks N     (whole-stream form: N chunks in one call)
     python bench.py --flatness     (300-chunk stream, per-chunk latency)
     python bench.py --overlap L    (L-layer chunk-step, cache writes on a second stream)
+    python bench.py --tune-table   (every launch configuration x split form, per shape)
 """
 from __future__ import annotations
 
@@ -392,6 +393,63 @@ def measure_stream(spec: synthetic.StreamSpec, steps: int, warmup: int, n_sets: 
     return res
 
 
+def tune_table(args) -> int:
+    """Per workload shape, one steady call of every (launch configuration,
+    split form) timed, and the choice kv_cache_autotune makes; one JSON line
+    per shape."""
+    import torch
+    from block_causal_kv_amd import KVCache
+    dev = torch.device("cuda", 0)
+    shapes = [synthetic.SPECS["720p"], synthetic.SPECS["mid"], synthetic.SPECS["long"],
+              synthetic.small_spec("d64", n_chunks=8, chunk_tokens=3600, cond_len=256, heads=48, head_dim=64,
+                                   window=4, seed=9),
+              synthetic.SPECS["fp8"],
+              synthetic.small_spec("long-fp8", n_chunks=12, chunk_tokens=3600, cond_len=256, heads=32,
+                                   head_dim=128, window=8, seed=3, kv_dtype="fp8")]
+
+    def dev_bf16(x):
+        return torch.from_numpy(synthetic.bf16_bits(x).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    for spec in shapes:
+        H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
+        x = synthetic.chunk_inputs(spec, 0)
+        q, k, v = dev_bf16(x.q[0]), dev_bf16(x.k[0]), dev_bf16(x.v[0])
+        kc, vc = dev_bf16(x.k_clean), dev_bf16(x.v_clean)
+        ck, cv = synthetic.cond_inputs(spec)
+        out = torch.empty((H, T, D), dtype=torch.bfloat16, device=dev)
+        cache = KVCache(T, spec.window, spec.n_sink, spec.cond_len, H, D, spec.kv_dtype)
+        cache.set_condition(dev_bf16(ck), dev_bf16(cv))
+        for _ in range(spec.n_sink + spec.window):
+            cache.append_chunk(kc, vc)
+        n_split = 2 if spec.kv_dtype == "fp8" else 4
+        cfgs = cache.configs()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = {}
+        for rnd in range(3):  # best of three rounds per candidate
+            for c in range(len(cfgs)):
+                for f in range(n_split):
+                    cache.config, cache.split = c, f
+                    cache.attention(q, k, v, out=out)
+                    e0.record()
+                    for _ in range(args.steps):
+                        cache.attention(q, k, v, out=out)
+                    e1.record()
+                    e1.synchronize()
+                    ms = e0.elapsed_time(e1) / args.steps
+                    best[(c, f)] = min(best.get((c, f), 1e30), ms)
+        cache.config, cache.split = 0, 0
+        chosen, _ = cache.autotune(q, k, v, out=out, reps=5)
+        win = min(best, key=best.get)
+        rec = {"shape": workload_name(spec), "kv_dtype": spec.kv_dtype, "H": H, "T": T, "D": D,
+               "kv_len": spec.steady_kv_len(), "calls_timed": args.steps,
+               "ms": {"c%d/s%d" % cf: round(ms, 4) for cf, ms in sorted(best.items())},
+               "configs": [list(x) for x in cfgs],
+               "fastest": "c%d/s%d" % win, "autotune_chose": {"config": chosen, "split": cache.split}}
+        print(json.dumps(rec), flush=True)
+        cache.close()
+    return 0
+
+
 def overlap_bench(args) -> int:
     """A multi-layer chunk-step (L layers of the 720p-shaped stream, bf16 or
     fp8 cache): each layer's two attention calls on stream A, then its clean
@@ -483,6 +541,9 @@ def main() -> int:
     ap.add_argument("--overlap", type=int, default=0,
                     help="time an L-layer chunk-step with each layer's cache write on a second stream "
                          "beside the next layer's attention, against the same work on one stream")
+    ap.add_argument("--tune-table", action="store_true",
+                    help="time every launch configuration and split form on several workload shapes "
+                         "(one JSON line per shape) instead of the throughput line")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the fp8-cache run that the default 720p line reports beside the headline")
     ap.add_argument("--no-autotune", action="store_true",
@@ -502,6 +563,8 @@ def main() -> int:
         return flatness(args)
     if args.overlap > 0:
         return overlap_bench(args)
+    if args.tune_table:
+        return tune_table(args)
     if args.chunks > 0:
         return whole_stream(args)
     spec = synthetic.SPECS[args.config]
@@ -546,10 +609,12 @@ def main() -> int:
     }
     if args.config == "720p" and not args.no_fp8:
         # the same stream with an E4M3 cache (fp8 MFMA for both products),
-        # timed after the headline run; reported beside it
+        # timed after the headline run and prepared the same way (the
+        # autotune's calls also bring the clock up after the host-side set-up,
+        # which a few warm-up steps alone do not); reported beside it
         f8 = synthetic.SPECS["fp8"]
-        n8 = max(5, args.steps // 2)
-        m8 = measure_stream(f8, n8, args.warmup, args.sets, False)
+        n8 = args.steps
+        m8 = measure_stream(f8, n8, args.warmup, args.sets, not args.no_autotune)
         a8 = float(np.mean(m8["attn_ms"]))
         fl8 = flop_per_call(f8)
         rec["fp8_kv"] = {"workload": workload_name(f8), "steps": n8,
@@ -558,7 +623,8 @@ def main() -> int:
                          "tflops_per_call": round(fl8 / (a8 * 1e-3) / 1e12, 2),
                          "frac_of_fp8_peak": round(fl8 / (a8 * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
                          "speedup_vs_bf16_call": round(attn_avg / a8, 4),
-                         "append_ms": round(float(np.mean(m8["app_ms"])), 4)}
+                         "append_ms": round(float(np.mean(m8["app_ms"])), 4),
+                         "kernel_config": m8["kernel_cfg"]}
     peaks = measure_peaks(stream) if not args.no_probes else None  # after the timed region
     if peaks is not None:
         peaks["attention_frac_of_measured_mfma"] = round(achieved / peaks["bf16_mfma_tflops"], 4)
