@@ -20,7 +20,8 @@
 //
 // Work decomposition
 //   One workgroup = 8 waves = one (head, query tile of up to 256 rows; the T
-//   rows of a head are cut into equal tiles); each wave owns 32 query rows and
+//   rows of a head are cut into full tiles and a shorter last one); each wave
+//   owns 32 query rows and
 //   keeps their Q in registers.  One workgroup per CU: every SIMD holds two of
 //   its waves, and one wave's MFMAs overlap the other's softmax arithmetic.
 //   The workgroup streams the head's keys in tiles of 64 through two LDS
@@ -1047,8 +1048,13 @@ constexpr LaunchCfg kCfg64[] = {{8, 1, kPingPong}, {4, 2, kLockstep}, {4, 3, kLo
 template <int D, int NW, int WGS, int SCHED>
 int launch_cfg(AttnArgs& a, hipStream_t stream) {
   using C = Cfg<D, NW, SCHED>;
+  // Full query tiles and a shorter last one rather than equal tiles: the
+  // waves of a workgroup meet at a barrier every phase, so a unit with one
+  // partly filled wave costs as much as a full one, while a last unit with
+  // few active waves costs less (720p: 14 x 256 + 16 rows per head instead of
+  // 15 x 240, 2.5 % faster at 720p and on the 300-chunk stream).
   a.q_tiles = (a.Tq + C::ROWS - 1) / C::ROWS;
-  a.q_rows = (a.Tq + a.q_tiles - 1) / a.q_tiles;  // equal tiles
+  a.q_rows = C::ROWS;
   const int units = a.H * a.q_tiles;
   int tiles = (a.T + C::BN - 1) / C::BN;
   for (int s = 0; s < a.nseg; ++s) tiles += (a.seg_len[s] + C::BN - 1) / C::BN;
@@ -1112,7 +1118,7 @@ int launch_chunks(AttnArgs& a, hipStream_t stream) {
   using C = Cfg<D, NW, SCHED>;
   a.Tq = a.T;
   a.q_tiles = (a.T + C::ROWS - 1) / C::ROWS;
-  a.q_rows = (a.T + a.q_tiles - 1) / a.q_tiles;  // equal tiles
+  a.q_rows = C::ROWS;  // full tiles and a shorter last one (as in the cache call)
   const int grid = a.H * a.n_chunks * a.q_tiles;
   a.xcd_units = 0;
   hipLaunchKernelGGL((attention_bf16_kernel<D, NW, WGS, SCHED, true>), dim3(grid), dim3(C::NT), 0, stream, a);

@@ -739,7 +739,7 @@ template <int D>
 int launch_fp8(AttnArgs& a, int config, hipStream_t stream) {
   using C = F8Cfg<D>;
   a.q_tiles = (a.Tq + C::ROWS - 1) / C::ROWS;
-  a.q_rows = (a.Tq + a.q_tiles - 1) / a.q_tiles;  // equal tiles
+  a.q_rows = C::ROWS;  // full tiles and a shorter last one (as in the bf16 kernel)
   const int units = a.H * a.q_tiles;
   int tiles = 0;
   for (int s = 0; s < a.nseg; ++s) tiles += (a.seg_len[s] + C::BN - 1) / C::BN;
