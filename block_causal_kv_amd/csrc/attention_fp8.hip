@@ -32,11 +32,15 @@
 // Layout: every segment (condition rows, each resident slot, and the current
 // chunk quantised into the spare slot) is its own segment because scales are
 // per chunk.  K codes [H][rows][D]; V codes transposed [H][D][rows]; segment
-// starts and lengths are multiples of 16 rows.  Schedule as in the bf16
-// kernel: one 8-wave workgroup per CU and (head, query tile of up to 256
-// rows), 64-key tiles loaded straight into double-buffered LDS (buffer_load
-// ... lds, spread over the S^T MFMAs), key-slice split of the last round
-// (slices leave partials that a second kernel merges).
+// starts and lengths are multiples of 16 rows.  Work as in the bf16 kernel:
+// one 8-wave workgroup per CU and (head, query tile of up to 256 rows; full
+// tiles and a shorter last one), 64-key tiles loaded straight into LDS
+// (buffer_load ... lds), key-slice split of the last round (slices leave
+// partials that a second kernel merges), units grouped by XCD.  Two
+// schedules of the key-tile loop: ping-pong (the default; two wave groups in
+// alternate MFMA and softmax phases over four LDS buffers, see the kernel)
+// and lockstep (every wave in the same phase, two buffers, the next tile's
+// loads spread over the S^T MFMAs).
 //
 // Key order: K rows are read so that in S^T's accumulator lane half hf holds
 // keys kb*32 + 16*hf + r in register r (16 consecutive keys per 32-key

@@ -282,8 +282,13 @@ int kvc_chunks_workspace_bytes(kvc_handle h, int n_chunks, size_t* out_bytes);
 
 /*
  * Launch configurations of the attention kernel (waves per workgroup x
- * workgroups resident per CU).  bf16 caches: 8x1 and 4x2 at D = 128, 8x1,
- * 4x2 and 4x3 at D = 64; fp8 caches: one.  Configuration 0 is the default.
+ * workgroups resident per CU x schedule of the key-tile loop).  bf16 caches:
+ * 0 8x1 ping-pong, 1 4x2 lockstep, 2 8x1 in-wave pipeline, 3 4x2 in-wave at
+ * D = 128; 0 8x1 ping-pong, 1 4x2 lockstep, 2 4x3 lockstep, 3 8x1 in-wave,
+ * 4 4x2 in-wave at D = 64.  fp8 caches: 0 8x1 ping-pong, 1 8x1 lockstep.
+ * kv_cache_config_info reports waves and workgroups only (configurations
+ * that differ in the schedule alone report the same pair).  Configuration 0
+ * is the default.
  * Which is fastest depends on H, T, the key count and D (how the units of
  * work fill the CUs' slots, how many workgroups share one head's K/V stream),
  * so it is measured rather than modelled.  Not described by the pages (they
