@@ -179,6 +179,16 @@ class KVCache:
         return out
 
     # ---- launch configurations of the attention kernel
+    def time_kernel(self, start=None, stop=None) -> None:
+        """Record the torch.cuda.Event pair (timing enabled, recorded at least
+        once so that it exists) around the attention kernel of every later call
+        (``kv_cache_time_kernel``); no arguments to stop."""
+        if (start is None) != (stop is None):
+            raise ValueError("give both events or neither")
+        sp = None if start is None else C.c_void_p(start.cuda_event)
+        ep = None if stop is None else C.c_void_p(stop.cuda_event)
+        check(self._lib.kv_cache_time_kernel(self._h, sp, ep))
+
     def configs(self) -> List[Tuple[int, int]]:
         """(waves per workgroup, workgroups per CU) of each configuration."""
         n = C.c_int()

@@ -48,6 +48,7 @@ SIGNATURES = {
                                                C.c_void_p, C.c_void_p, C.c_float, C.c_void_p, C.c_size_t,
                                                C.c_void_p]),
     "kvc_chunks_workspace_bytes": (C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_size_t)]),
+    "kv_cache_time_kernel": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
     "kv_cache_pool_view": (C.c_int, [C.c_void_p, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p),
                                      C.POINTER(C.c_void_p), _I64P, _IP]),
     "kvc_table_create": (C.c_int, [C.c_int, C.c_int, C.POINTER(C.c_void_p)]),

@@ -1103,8 +1103,10 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
   // XCD grouping when both blocks of the schedule divide evenly over the XCDs
   a.xcd_units = units % 8 == 0 && a.n_whole % 8 == 0 && n_ranges % 8 == 0 ? units / 8 : 0;
   const int grid = a.grid_whole + 8 * ((a.n_ranges + 7) / 8);
+  if (a.ev_start != nullptr && hipEventRecord((hipEvent_t)a.ev_start, stream) != hipSuccess) return -1;
   hipLaunchKernelGGL((attention_bf16_kernel<D, NW, WGS, SCHED, false>), dim3(grid), dim3(C::NT), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return -1;
+  if (a.ev_stop != nullptr && hipEventRecord((hipEvent_t)a.ev_stop, stream) != hipSuccess) return -1;
   // ranges that are not exactly the last round's units split some of them
   if (n_ranges > 0 && n_ranges != rest) {
     hipLaunchKernelGGL((merge_pieces_kernel<D, NW>), dim3(rest * NW), dim3(64), 0, stream, a);

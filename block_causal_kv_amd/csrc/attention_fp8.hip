@@ -774,11 +774,13 @@ int launch_fp8(AttnArgs& a, int config, hipStream_t stream) {
   // XCD grouping when the whole and the split units divide evenly over the XCDs
   a.xcd_units = units % 8 == 0 && a.n_whole % 8 == 0 ? units / 8 : 0;
   const int grid = a.grid_whole + 8 * ((a.rest * a.slices + 7) / 8);
+  if (a.ev_start != nullptr && hipEventRecord((hipEvent_t)a.ev_start, stream) != hipSuccess) return -1;
   if (kF8Cfg[config] == kF8PingPong)
     hipLaunchKernelGGL((attention_fp8_kernel<D, kF8PingPong>), dim3(grid), dim3(C::NT), 0, stream, a);
   else
     hipLaunchKernelGGL((attention_fp8_kernel<D, kF8Lockstep>), dim3(grid), dim3(C::NT), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return -1;
+  if (a.ev_stop != nullptr && hipEventRecord((hipEvent_t)a.ev_stop, stream) != hipSuccess) return -1;
   if (a.slices > 1) {
     hipLaunchKernelGGL((merge_slices_kernel<D>), dim3(a.rest * C::NW), dim3(64), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return -1;

@@ -66,6 +66,8 @@ struct kvc_cache {
   int config = 0;  // bf16 attention launch configuration (kv_cache_set_config)
   int split = 0;   // split of a partly filled last round of query tiles (kv_cache_set_split)
   bool poison = false;  // debug: fill slots freed by kv_cache_evict / kv_cache_reset with NaN
+  void* time_start = nullptr;  // kv_cache_time_kernel: events around the attention kernel, or null
+  void* time_stop = nullptr;
   // Layers.  The root handle owns the pools, the slot table and the layer
   // views; a view (kv_cache_layer) points at its layer's heads in the pools.
   int layers = 1;
@@ -236,6 +238,8 @@ int attention_call(kvc_cache* h, int n_q, const void* q, const void* k_cur, cons
   a.ws_o = ws_o;
   a.ws_ml = ws_ml;
   a.split = h->split;
+  a.ev_start = h->time_start;
+  a.ev_stop = h->time_stop;
   hipStream_t st = (hipStream_t)stream;
   if (fp8) {
     // every chunk has its own scales: one segment per block, the current chunk
@@ -795,6 +799,16 @@ int sink_window_attention_chunks(kvc_handle h, int n_chunks, const void* q, cons
     return fail(KVC_ERR_HIP, "sink_window_attention_chunks: transpose launch failed");
   if (kvc::launch_attention_chunks_bf16(a, h->D, h->config, (hipStream_t)stream) != 0)
     return fail(KVC_ERR_HIP, "sink_window_attention_chunks: launch failed");
+  return KVC_OK;
+}
+
+int kv_cache_time_kernel(kvc_handle h, void* start_event, void* stop_event) {
+  g_last_error.clear();
+  if (!h) return fail(KVC_ERR_INVALID, "kv_cache_time_kernel: handle is NULL");
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(KVC_ERR_INVALID, "kv_cache_time_kernel: give both events or neither");
+  h->time_start = start_event;
+  h->time_stop = stop_event;
   return KVC_OK;
 }
 

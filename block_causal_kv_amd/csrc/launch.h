@@ -59,6 +59,10 @@ struct AttnArgs {
   // XCD serves units / 8 consecutive units (H / 8 heads when H is a multiple
   // of 8) and a head's K/V is fetched into one XCD's L2 only.
   int xcd_units;
+  // measurement (host side only): events recorded right before and after the
+  // attention kernel's launch, or null
+  void* ev_start;
+  void* ev_stop;
   float* ws_o;     // partial O^T of the slices: [piece][wave][register][lane]
   float* ws_ml;    // partial (max, sum): [piece][wave][2][lane]
   int num_cus;

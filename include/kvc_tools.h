@@ -1,9 +1,10 @@
 /*
  * kvc_tools.h - inspection and measurement entry points of libkvc.so that are
  * not part of the method: device addresses of a cache's pool (for tests that
- * read back stored codes and scales) and two probes that measure this
- * device's sustained MFMA and copy rates (for reporting a kernel's fraction
- * of what the chip sustains).  Same conventions and error codes as kvc.h.
+ * read back stored codes and scales), two probes that measure this device's
+ * sustained MFMA and copy rates (for reporting a kernel's fraction of what
+ * the chip sustains), and events around the attention kernel alone (for its
+ * launch duration).  Same conventions and error codes as kvc.h.
  */
 #ifndef KVC_TOOLS_H
 #define KVC_TOOLS_H
@@ -46,6 +47,19 @@ int kvc_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
  */
 int kv_cache_pool_view(kvc_handle h, const void** k_pool, const void** v_pool, const float** scales,
                        int64_t* rows, int* blocks);
+
+/*
+ * kv_cache_time_kernel - on every later attention call through this handle
+ * (sink_window_attention, _rows, _noalloc), record start_event right before
+ * and stop_event right after the attention kernel itself, on the call's
+ * stream: not around the call's other kernels (the v_cur transpose or the
+ * fp8 quantisation before it, the merge of split units after it).  The events
+ * are the caller's (hipEvent_t, created with timing enabled), and the caller
+ * reads the duration with hipEventElapsedTime once the call is done; pass
+ * NULL for both to stop.  Measurement tooling.  Errors: INVALID (one event
+ * NULL and the other not).
+ */
+int kv_cache_time_kernel(kvc_handle h, void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }

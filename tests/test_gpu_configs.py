@@ -122,3 +122,39 @@ def test_whole_stream_other_config(cfg):
     spec = synthetic.small_spec("ragged_multi_c", n_chunks=5, chunk_tokens=604, cond_len=44, heads=6,
                                 head_dim=128, window=2, seed=61, outlier_frac=0.01)
     run_chunks(spec, 5, full_mask=False, config=cfg)
+
+
+def test_kernel_timing_events():
+    """kv_cache_time_kernel records the caller's events around the attention
+    kernel alone: its duration is positive and below the whole call's, and
+    after the events are withdrawn later calls leave them untouched."""
+    import torch
+    from block_causal_kv_amd import KVCache
+    spec = synthetic.small_spec("timing", n_chunks=4, chunk_tokens=600, cond_len=64, heads=8, head_dim=128,
+                                window=2, seed=62)
+    H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
+    cache = KVCache(T, spec.window, spec.n_sink, spec.cond_len, H, D)
+    ck, cv = synthetic.cond_inputs(spec)
+    cache.set_condition(to_dev(ck), to_dev(cv))
+    for c in range(3):
+        x = synthetic.chunk_inputs(spec, c)
+        cache.append_chunk(to_dev(x.k_clean), to_dev(x.v_clean))
+    x = synthetic.chunk_inputs(spec, 3)
+    q, k, v = to_dev(x.q[0]), to_dev(x.k[0]), to_dev(x.v[0])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev[2:]:
+        e.record()  # exists before the library records it
+    cache.attention(q, k, v)  # warm-up
+    ev[0].record()
+    cache.time_kernel(ev[2], ev[3])
+    cache.attention(q, k, v)
+    ev[1].record()
+    cache.time_kernel()
+    torch.cuda.synchronize()
+    call_ms, kern_ms = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])
+    say("call %.4f ms, kernel %.4f ms" % (call_ms, kern_ms))
+    assert 0 < kern_ms < call_ms
+    cache.attention(q, k, v)
+    torch.cuda.synchronize()
+    assert ev[2].elapsed_time(ev[3]) == kern_ms
+    cache.close()
