@@ -144,6 +144,73 @@ def cpu_baseline(spec: synthetic.StreamSpec, budget_s: float = 12.0) -> dict:
                                            spec.steps * flop_per_call(spec) / (flop / dt) * 1e3)}
 
 
+def oracle_times(args) -> int:
+    """The CPU oracle's own cost, one JSON line per case (no GPU is touched):
+    the tiny and mid streams in full (every chunk's calls), and one 720p head
+    at the first steady chunk (c = n_sink + W, whose concatenated sequence is
+    exactly the resident set) and at the stream's last chunk, where the
+    explicit mask spans the whole history and the oracle's work grows with
+    it.  The 720p cases take the first rows_720p query rows of the head (the
+    per-row cost does not depend on the row)."""
+    from oracle.stream import attend_chunk
+    host = host_cpu()
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+
+    def emit(case, spec, seconds, calls, visible_flop, mask_flop, note):
+        print(json.dumps({"case": case, "workload": workload_name(spec), "seconds": round(seconds, 3),
+                          "calls": calls, "visible_tflop": visible_flop / 1e12,
+                          "oracle_tflop_evaluated": mask_flop / 1e12,
+                          "visible_tflop_per_s": round(visible_flop / seconds / 1e12, 4),
+                          "threads": int(threads), "nproc": host["nproc"], "cpu_model": host["cpu_model"],
+                          "note": note}), flush=True)
+
+    for name in ("tiny", "mid"):
+        spec = synthetic.SPECS[name]
+        ck, cv = synthetic.cond_inputs(spec)
+        xs = {}
+        t0 = time.perf_counter()
+        vis = mask = 0.0
+        calls = 0
+        for c in range(spec.n_chunks):
+            xs[c] = synthetic.chunk_inputs(spec, c)
+            n_all = spec.cond_len + (c + 1) * spec.chunk_tokens
+            n_vis = spec.cond_len + spec.chunk_tokens * (1 + len(
+                [j for j in range(c) if j < spec.n_sink or j >= c - spec.window]))
+            for s in range(spec.steps):
+                attend_chunk(c, xs[c].q[s], xs[c].k[s], xs[c].v[s], lambda j: xs[j].k_clean,
+                             lambda j: xs[j].v_clean, ck, cv, spec.window, spec.n_sink, spec.scale)
+                f = 4.0 * spec.heads * spec.chunk_tokens * spec.head_dim
+                vis += f * n_vis
+                mask += f * n_all
+                calls += 1
+        emit(name + " stream", spec, time.perf_counter() - t0, calls, vis, mask,
+             "every chunk of the stream, all heads and rows (input generation included)")
+
+    spec = synthetic.SPECS["720p"]
+    rows = list(range(min(args.rows_720p, spec.chunk_tokens)))
+    ck, cv = synthetic.cond_inputs(spec, heads=1)
+    for c in (spec.n_sink + spec.window, spec.n_chunks - 1):
+        clean = {j: synthetic.chunk_inputs(spec, j, heads=1, clean_only=True)
+                 for j in range(c) if j < spec.n_sink or j >= c - spec.window}
+        x = synthetic.chunk_inputs(spec, c, heads=1)
+        zero = np.zeros_like(x.k[0])  # chunks outside the window: masked, values never used
+        t0 = time.perf_counter()
+        attend_chunk(c, x.q[0], x.k[0], x.v[0], lambda j: clean[j].k_clean if j in clean else zero,
+                     lambda j: clean[j].v_clean if j in clean else zero, ck, cv, spec.window, spec.n_sink,
+                     spec.scale, rows=rows)
+        dt = time.perf_counter() - t0
+        f = 4.0 * len(rows) * spec.head_dim
+        n_all = spec.cond_len + (c + 1) * spec.chunk_tokens
+        emit("720p chunk %d" % c, spec, dt, 1, f * spec.steady_kv_len(), f * n_all,
+             "one head, %d of %d query rows; a whole call (%d heads, all rows) is %.0fx this"
+             % (len(rows), spec.chunk_tokens, spec.heads, spec.heads * spec.chunk_tokens / len(rows)))
+    return 0
+
+
 def flatness_stats(ms, first_steady: int) -> dict:
     """Flatness of per-chunk latency over the steady chunks (those whose cache
     holds the sink and a full window): p99/p50, least-squares slope over the
@@ -561,7 +628,14 @@ def main() -> int:
                     help="keep the default launch configuration instead of timing each once before the run")
     ap.add_argument("--chunks", type=int, default=0,
                     help="time the whole-stream form instead: every chunk of an N-chunk stream in one call")
+    ap.add_argument("--oracle-times", action="store_true",
+                    help="time the CPU oracle alone (tiny and mid streams in full, a 720p head at a "
+                         "steady chunk and at the last chunk) and print one JSON line per case")
+    ap.add_argument("--rows-720p", type=int, default=900,
+                    help="query rows of the 720p head that --oracle-times computes")
     args = ap.parse_args()
+    if args.oracle_times:
+        return oracle_times(args)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: attention shards by heads with no exchange, so "
               "N GPUs would each run this same kernel on H/N heads; no multi-GPU run is made.",

@@ -494,7 +494,7 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
       // ---- ping-pong schedule.  SIMD s holds wave s (group A) and wave s + 4
       // (group B).  Per key tile j every wave runs two phases:
       //   X_j: S(j) = K(j) Q^T and O^T += V(j-1)^T P(j-1)^T (32 MFMAs), then
-      //        the row max of S(j)
+      //        the row sum of P(j-1) and the row max of S(j)
       //   Y_j: the loads of tile j + 2, the softmax of S(j) -> P(j)
       // Group B runs one phase behind group A and a workgroup barrier ends
       // every phase, so on each SIMD one wave streams MFMAs while the other
@@ -529,16 +529,23 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
       bf16x8 pb[C::KB][2];
       float mx = 0.f;                 // row max of S(j), scaled (X_j -> Y_j)
       // X: S(j) = K(j) Q^T from buffer j % 4 (DO_S), then O^T += V(j-1)^T
-      // P(j-1)^T from buffer (j-1) % 4 (DO_PV), then the row max of S(j).
+      // P(j-1)^T from buffer (j-1) % 4 (DO_PV), then the row sum of P(j-1)
+      // (DO_PV) and the row max of S(j) (DO_S).
       // The buffer offsets are wave-uniform multiples of the tile size, OR-ed
       // into the lane addresses (a lane's K address lies below one tile; its
       // V^T address is the V^T region's base, a multiple of four tiles, plus
       // less than one tile: the OR is an add).  Operand reads run RA ahead of their MFMAs
       // through a ring of registers; sched_barrier keeps that order (the
       // scheduler would otherwise chain MFMAs of one accumulator back to back
-      // and wait on single reads).  The row max sits here rather than in Y:
-      // this wave waits at the barrier anyway while the other one runs the
-      // exponentials, which are the longer half.
+      // and wait on single reads).  The row sum and the row max sit here
+      // rather than in Y: this wave waits at the barrier anyway while the
+      // other one runs the exponentials, which are the longer half.  The row
+      // sum is a dot product of P's bf16 pairs with (1, 1) (v_dot2c), an
+      // instruction that waits for the MFMA pipe: in Y, beside the other
+      // wave's MFMA stream, each one cost tens of cycles of the critical
+      // phase (720p call 4 %, 300-chunk-stream call 8 % faster with the
+      // row sum here).  l then holds P(j-1)'s sum from X_j on: Y_j's rescale
+      // scales it with O^T, whose PV(j-1) term X_j has just added.
       auto phase_x = [&](auto do_s, auto do_pv, int j) {
         constexpr bool DO_S = decltype(do_s)::value, DO_PV = decltype(do_pv)::value;
         constexpr int NS = DO_S ? C::KB * C::DS : 0;              // S: k-step outer, key block inner
@@ -583,6 +590,18 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
           __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_setprio(0);
+        if constexpr (DO_PV) {  // l += row sum of the same bf16 P(j-1) the PV MFMAs used
+          float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+          for (int kh = 0; kh < 2 * C::KB; ++kh) {
+            const u32x4 w = __builtin_bit_cast(u32x4, pb[kh >> 1][kh & 1]);
+            r0 = sum2_bf16(w[0], r0);
+            r1 = sum2_bf16(w[1], r1);
+            r0 = sum2_bf16(w[2], r0);
+            r1 = sum2_bf16(w[3], r1);
+          }
+          l_run += r0 + r1;
+        }
         if constexpr (DO_S) {
           const int valid = uniform(min(C::BN, ccur.len - ccur.off));
           if (valid < C::BN) mask_tail(sacc, valid);
@@ -618,15 +637,11 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
 #pragma unroll
               for (int k = 0; k < 16; ++k) oacc[db][k] *= alpha;
           }
-          // P = exp2(s*c - m) as bf16; the row sum adds the same bf16 values
-          // that enter the PV product (dot product with (1, 1), four
-          // independent chains).  The dot product waits for the MFMA pipe when
-          // the other wave of the SIMD streams MFMAs back to back (a probe
-          // measured about 70 cycles instead of 5.5), but in this schedule it
-          // finds the gaps between that wave's MFMAs: summing the widened
-          // values with plain adds instead (three times the instructions)
-          // measured 3 % slower.
-          float rs[4] = {0.f, 0.f, 0.f, 0.f};
+          // P = exp2(s*c - m) as bf16 (its row sum is taken in X_{j+1}).
+          // Also moving the bf16 packs into X (P kept in fp32 until then)
+          // measured from 1 % faster to 4 % slower by shape and placement,
+          // and the rescale decision with the scale-and-subtract 5-9 %
+          // slower: plain VALU work in X takes issue slots from this phase.
 #pragma unroll
           for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -637,12 +652,10 @@ __global__ __launch_bounds__(NW * 64, WGS) void attention_bf16_kernel(AttnArgs a
                 const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][h2 * 8 + 2 * k], c, -m_run));
                 const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][h2 * 8 + 2 * k + 1], c, -m_run));
                 w[k] = pack_bf16(p0, p1);
-                rs[2 * h2 + (k & 1)] = sum2_bf16(w[k], rs[2 * h2 + (k & 1)]);
               }
               const u32x4 wv = {w[0], w[1], w[2], w[3]};
               pb[kb][h2] = __builtin_bit_cast(bf16x8, wv);
             }
-          l_run += (rs[0] + rs[1]) + (rs[2] + rs[3]);
         }
         ccur = advance(ccur);
         __builtin_amdgcn_s_setprio(0);
