@@ -19,6 +19,7 @@ oracle on a bounded sample of the same call.
     python bench.py --flatness     (300-chunk stream, per-chunk latency)
     python bench.py --overlap L    (L-layer chunk-step, cache writes on a second stream)
     python bench.py --tune-table   (every launch configuration x split form, per shape)
+    python bench.py --oracle-times (the CPU oracle alone: tiny and mid streams, 720p heads)
 """
 from __future__ import annotations
 
@@ -284,8 +285,9 @@ def flatness(args) -> int:
 
 def measure_peaks(stream) -> dict:
     """Sustained rates of this device from the library's probes: bf16 MFMA
-    (v_mfma_f32_32x32x16_bf16, independent accumulators, 2 waves per SIMD) and a
-    16-byte-vector device copy of 1 GiB (read + write bytes).  Best of 3."""
+    (v_mfma_f32_32x32x16_bf16, independent accumulators, 2 waves per SIMD), a
+    16-byte-vector device copy of 1 GiB (read + write bytes) and 1 GiB read
+    into LDS by the attention kernels' direct buffer-to-LDS loads.  Best of 3."""
     import torch
     from block_causal_kv_amd import _lib
     import ctypes as C
@@ -297,7 +299,7 @@ def measure_peaks(stream) -> dict:
     dst = torch.empty_like(src)
     sp = C.c_void_p(stream.cuda_stream)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    best_mfma, best_copy = 0.0, 0.0
+    best_mfma, best_copy, best_lds = 0.0, 0.0, 0.0
     for _ in range(3):
         e0.record(stream)
         _lib.check(lib.kvc_probe_mfma_bf16(C.c_void_p(sink.data_ptr()), blocks, iters, sp))
@@ -309,10 +311,17 @@ def measure_peaks(stream) -> dict:
         e1.record(stream)
         e1.synchronize()
         best_copy = max(best_copy, 2.0 * src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        e0.record(stream)
+        _lib.check(lib.kvc_probe_lds_load(C.c_void_p(src.data_ptr()), src.numel(), sp))
+        e1.record(stream)
+        e1.synchronize()
+        best_lds = max(best_lds, src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     del src, dst, sink
     return {"bf16_mfma_tflops": round(best_mfma, 1), "hbm_copy_gbps": round(best_copy, 1),
+            "hbm_to_lds_gbps": round(best_lds, 1),
             "what": "library probes: %d workgroups x 4 waves x %d x 4 independent 32x32x16 bf16 MFMAs; "
-                    "1 GiB device copy (read + write bytes); best of 3" % (blocks, iters)}
+                    "1 GiB device copy (read + write bytes); 1 GiB read into LDS by direct buffer-to-LDS "
+                    "loads; best of 3" % (blocks, iters)}
 
 
 def stream_flop(spec: synthetic.StreamSpec, n: int) -> float:
@@ -615,7 +624,8 @@ def main() -> int:
                     help="stream the 300-chunk long config from an empty cache and report per-chunk "
                          "latency flatness and device memory instead of the throughput line")
     ap.add_argument("--no-probes", action="store_true",
-                    help="skip the MFMA and copy probes that report this device's sustained rates")
+                    help="skip the MFMA, copy and direct-to-LDS load probes that report this device's "
+                         "sustained rates")
     ap.add_argument("--overlap", type=int, default=0,
                     help="time an L-layer chunk-step with each layer's cache write on a second stream "
                          "beside the next layer's attention, against the same work on one stream")

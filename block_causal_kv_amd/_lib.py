@@ -31,6 +31,7 @@ SIGNATURES = {
                                          C.POINTER(C.c_int64)]),
     "kvc_probe_mfma_bf16": (C.c_int, [C.c_void_p, C.c_int, C.c_int, C.c_void_p]),
     "kvc_probe_copy": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "kvc_probe_lds_load": (C.c_int, [C.c_void_p, C.c_size_t, C.c_void_p]),
     "sink_window_attention_noalloc": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p,
                                                 C.c_void_p, C.c_float, C.c_void_p]),
     "sink_window_attention_rows": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p,

@@ -739,6 +739,19 @@ int kvc_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
   return KVC_OK;
 }
 
+int kvc_probe_lds_load(const void* src, size_t bytes, void* stream) {
+  g_last_error.clear();
+  if (!src || bytes == 0 || bytes % 4096 != 0)
+    return fail(KVC_ERR_INVALID, "kvc_probe_lds_load: need src and a positive multiple of 4096 bytes");
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return fail(KVC_ERR_HIP, "kvc_probe_lds_load: device query failed");
+  if (kvc::launch_lds_load_probe(src, (int64_t)bytes, cus, (hipStream_t)stream) != 0)
+    return fail(KVC_ERR_HIP, "kvc_probe_lds_load: launch failed (or more than 2 GiB per workgroup)");
+  return KVC_OK;
+}
+
 int kvc_chunks_workspace_bytes(kvc_handle h, int n_chunks, size_t* out_bytes) {
   g_last_error.clear();
   if (!h || !out_bytes) return fail(KVC_ERR_INVALID, "kvc_chunks_workspace_bytes: NULL handle or output");

@@ -143,5 +143,6 @@ int launch_quantize_fp8(const uint16_t* k, const uint16_t* v, int H, int rows, i
 // Measurement probes (csrc/probes.hip).
 int launch_mfma_probe(float* sink, int blocks, int iters, hipStream_t stream);
 int launch_copy_probe(const void* src, void* dst, int64_t bytes, int num_cus, hipStream_t stream);
+int launch_lds_load_probe(const void* src, int64_t bytes, int num_cus, hipStream_t stream);
 
 }  // namespace kvc

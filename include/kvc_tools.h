@@ -1,10 +1,10 @@
 /*
  * kvc_tools.h - inspection and measurement entry points of libkvc.so that are
  * not part of the method: device addresses of a cache's pool (for tests that
- * read back stored codes and scales), two probes that measure this device's
- * sustained MFMA and copy rates (for reporting a kernel's fraction of what
- * the chip sustains), and events around the attention kernel alone (for its
- * launch duration).  Same conventions and error codes as kvc.h.
+ * read back stored codes and scales), three probes that measure this device's
+ * sustained MFMA, copy and direct-to-LDS load rates (for reporting a kernel's
+ * fraction of what the chip sustains), and events around the attention kernel
+ * alone (for its launch duration).  Same conventions and error codes as kvc.h.
  */
 #ifndef KVC_TOOLS_H
 #define KVC_TOOLS_H
@@ -25,11 +25,16 @@ extern "C" {
  * thread to the device array sink [blocks * 256]: the sustained rate of the
  * attention kernel's MFMA on this device.  kvc_probe_copy copies `bytes`
  * (a multiple of 16) from src to dst (device pointers) with 16-byte loads and
- * stores.  Both are asynchronous on `stream`; the caller times them.
- * Errors: INVALID, HIP.
+ * stores.  kvc_probe_lds_load reads `bytes` (a positive multiple of 4096)
+ * from src (device pointer) into LDS with the direct buffer-to-LDS loads the
+ * attention kernels stream their K/V tiles with (16 bytes per lane, each
+ * byte once; nothing is written to memory): that load path's rate, and the
+ * reference for what memory counters report for it.  All three are
+ * asynchronous on `stream`; the caller times them.  Errors: INVALID, HIP.
  */
 int kvc_probe_mfma_bf16(float* sink, int blocks, int iters, void* stream);
 int kvc_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+int kvc_probe_lds_load(const void* src, size_t bytes, void* stream);
 
 /*
  * kv_cache_pool_view - device addresses of the pool, for inspection (tests,

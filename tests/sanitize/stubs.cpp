@@ -42,4 +42,5 @@ int launch_quantize_fp8(const uint16_t*, const uint16_t*, int, int, int, uint32_
 }
 int launch_mfma_probe(float*, int, int, hipStream_t) { return -1; }
 int launch_copy_probe(const void*, void*, int64_t, int, hipStream_t) { return -1; }
+int launch_lds_load_probe(const void*, int64_t, int, hipStream_t) { return -1; }
 }  // namespace kvc

@@ -64,6 +64,12 @@ def test_create_rejects_bad_arguments_without_touching_the_gpu():
     n = C.c_size_t(7)
     assert lib.kvc_chunks_workspace_bytes(None, 2, C.byref(n)) == _lib.KVC_ERR_INVALID
     assert n.value == 7
+    # the probes validate their arguments before any device query
+    assert lib.kvc_probe_lds_load(None, 4096, None) == _lib.KVC_ERR_INVALID
+    assert lib.kvc_probe_lds_load(C.c_void_p(4096), 4095, None) == _lib.KVC_ERR_INVALID
+    assert lib.kvc_probe_lds_load(C.c_void_p(4096), 0, None) == _lib.KVC_ERR_INVALID
+    assert lib.kvc_probe_copy(None, None, 16, None) == _lib.KVC_ERR_INVALID
+    assert lib.kvc_probe_mfma_bf16(None, 1, 1, None) == _lib.KVC_ERR_INVALID
 
 
 @pytest.mark.parametrize("W,S", [(4, 1), (8, 1), (1, 1), (3, 2), (5, 0)])
