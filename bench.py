@@ -77,10 +77,10 @@ def kernel_sha() -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def measured_traffic(config: str, launch_config: int):
-    """HBM bytes per attention launch of the given launch configuration from
-    the committed rocprofv3 counter summary, if it was taken on the current
-    kernel source; else None."""
+def measured_traffic(config: str, launch_config: int, split: int = 0):
+    """HBM bytes per attention launch of the given launch configuration and
+    split form from the committed rocprofv3 counter summary, if it was taken
+    on the current kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -88,7 +88,10 @@ def measured_traffic(config: str, launch_config: int):
         return None
     if t.get("kernel_sha") != kernel_sha() or t.get("config") != config:
         return None
-    e = t.get("by_launch_config", {}).get(str(launch_config))
+    if split == 0:
+        e = t.get("by_launch_config", {}).get(str(launch_config))
+    else:
+        e = t.get("by_config_split", {}).get(str(launch_config), {}).get(str(split))
     return None if e is None else e.get("hbm_bytes_per_launch")
 
 
@@ -397,7 +400,8 @@ def whole_stream(args) -> int:
     return 0
 
 
-def measure_stream(spec: synthetic.StreamSpec, steps: int, warmup: int, n_sets: int, autotune: bool) -> dict:
+def measure_stream(spec: synthetic.StreamSpec, steps: int, warmup: int, n_sets: int, autotune: bool,
+                   split: int = -1) -> dict:
     """Time ``steps`` steady chunk-steps of ``spec`` (attention calls + clean
     append) after ``warmup`` untimed ones; inputs resident in HBM first."""
     import torch
@@ -447,9 +451,11 @@ def measure_stream(spec: synthetic.StreamSpec, steps: int, warmup: int, n_sets: 
         s0 = sets[0]
         best, tms = cache.autotune(s0["q"][0], s0["k"][0], s0["v"][0], out=out, reps=5, stream=stream)
         tuned = {"chosen": best, "ms_per_config": [round(t, 4) for t in tms]}
+    if split >= 0:  # a forced split form of the last round (after the autotune, if any)
+        cache.split = split
     cfgs = cache.configs()
     kernel_cfg = {"id": cache.config, "waves_per_workgroup": cfgs[cache.config][0],
-                  "workgroups_per_cu": cfgs[cache.config][1], "autotune": tuned}
+                  "workgroups_per_cu": cfgs[cache.config][1], "split_form": cache.split, "autotune": tuned}
     for i in range(warmup):
         chunk_step(i)
     torch.cuda.synchronize()
@@ -472,7 +478,7 @@ def measure_stream(spec: synthetic.StreamSpec, steps: int, warmup: int, n_sets: 
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     cache.time_kernel()
-    res = {"elapsed": elapsed, "config": cache.config, "kernel_cfg": kernel_cfg,
+    res = {"elapsed": elapsed, "config": cache.config, "split": cache.split, "kernel_cfg": kernel_cfg,
            "attn_ms": [e[0][s].elapsed_time(e[1][s]) for e in evs for s in range(spec.steps)],
            "kernel_ms": [e[4][s][0].elapsed_time(e[4][s][1]) for e in evs for s in range(spec.steps)],
            "app_ms": [e[2].elapsed_time(e[3]) for e in evs], "stream": stream}
@@ -508,7 +514,7 @@ def tune_table(args) -> int:
         cache.set_condition(dev_bf16(ck), dev_bf16(cv))
         for _ in range(spec.n_sink + spec.window):
             cache.append_chunk(kc, vc)
-        n_split = 2 if spec.kv_dtype == "fp8" else 4
+        n_split = 2 if spec.kv_dtype == "fp8" else 5
         cfgs = cache.configs()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         best = {}
@@ -638,6 +644,10 @@ def main() -> int:
                     help="keep the default launch configuration instead of timing each once before the run")
     ap.add_argument("--chunks", type=int, default=0,
                     help="time the whole-stream form instead: every chunk of an N-chunk stream in one call")
+    ap.add_argument("--split", type=int, default=-1,
+                    help="force the split form of the last round of query tiles in the headline run "
+                         "(kv_cache_set_split: 0 cost model, 1 none, 2 aligned slices, 3 one range per slot, "
+                         "4 whole heads)")
     ap.add_argument("--oracle-times", action="store_true",
                     help="time the CPU oracle alone (tiny and mid streams in full, a 720p head at a "
                          "steady chunk and at the last chunk) and print one JSON line per case")
@@ -664,7 +674,7 @@ def main() -> int:
         return whole_stream(args)
     spec = synthetic.SPECS[args.config]
     H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
-    m = measure_stream(spec, args.steps, args.warmup, args.sets, not args.no_autotune)
+    m = measure_stream(spec, args.steps, args.warmup, args.sets, not args.no_autotune, args.split)
     stream, elapsed, kernel_cfg = m["stream"], m["elapsed"], m["kernel_cfg"]
     attn_ms, app_ms = m["attn_ms"], m["app_ms"]
     ms_step = elapsed * 1e3 / args.steps
@@ -674,7 +684,7 @@ def main() -> int:
     kern_avg = float(np.mean(m["kernel_ms"]))  # the attention kernel alone (events around its launch)
     achieved = fl_call / (kern_avg * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if spec.kv_dtype == "fp8" else PEAK_BF16_TFLOPS
-    traffic = measured_traffic(args.config, m["config"]) if spec.kv_dtype == "bf16" else None
+    traffic = measured_traffic(args.config, m["config"], m["split"]) if spec.kv_dtype == "bf16" else None
     app_bytes = 2.0 * 2 * H * T * D * (1 if spec.kv_dtype == "fp8" else 2)  # K+V read and written
     rec = {
         "metric": METRIC,

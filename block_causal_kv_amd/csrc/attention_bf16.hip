@@ -88,6 +88,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "attention_common.h"
@@ -1105,10 +1106,32 @@ int launch_cfg(AttnArgs& a, hipStream_t stream) {
   const int slots = WGS * a.num_cus;
   int rest = a.ws_o == nullptr ? 0 : units % slots;
   int n_ranges = 0;
-  if (rest > 0) {
+  // Form 4, whole heads: equal query tiles, and on each XCD the heads whose
+  // tiles fit one round of its slots run whole while the tiles of its other
+  // heads are cut into aligned key slices (every slice of a head in step), so
+  // a head's K/V is streamed by the tiles of one round only: less traffic
+  // past L2 than the other forms, at the cost of equal tiles and of a split
+  // round that the slices may not fill.  Where the heads do not divide over
+  // the XCDs, or no head fits one XCD's slots, the cost model decides.
+  const int hpx = a.H / 8, spx = slots / 8;
+  if (a.split == 4 && a.ws_o != nullptr && a.H % 8 == 0 && slots % 8 == 0 && a.q_tiles <= spx) {
+    a.q_rows = (a.Tq + a.q_tiles - 1) / a.q_tiles;
+    const int whole = std::min(hpx, spx / a.q_tiles);  // whole heads per XCD
+    rest = units - 8 * whole * a.q_tiles;
+    if (rest > 0) {
+      // slices per split unit: the XCD's slots over its split units, at most
+      // one per key tile; below 2 every unit runs whole
+      const int s = std::min(spx / ((hpx - whole) * a.q_tiles), tiles);
+      if (s < 2)
+        rest = 0;
+      else
+        n_ranges = rest * s;  // aligned: range r is slice r % s of split unit r / s
+    }
+  } else if (rest > 0) {
     const int s = slots / rest;
-    // a.split picks the form (measured by kv_cache_autotune); 0 = the cost model
-    int form = a.split;
+    // a.split picks the form (measured by kv_cache_autotune); 0 (and 4 where
+    // it does not apply) = the cost model
+    int form = a.split == 4 ? 0 : a.split;
     if (form == 0) {
       const double aligned = 1.0 / s + (s > 1 ? 0.005 * s : 0.0);
       const double unaligned = (double)rest / slots + 0.08;

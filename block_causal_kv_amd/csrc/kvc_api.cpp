@@ -633,7 +633,7 @@ int kv_cache_get_config(kvc_handle h, int* out_id) {
 int kv_cache_set_split(kvc_handle h, int form) {
   g_last_error.clear();
   if (!h) return fail(KVC_ERR_INVALID, "kv_cache_set_split: handle is NULL");
-  const int n = h->kv_dtype == KVC_KV_FP8 ? 2 : 4;
+  const int n = h->kv_dtype == KVC_KV_FP8 ? 2 : 5;
   if (form < 0 || form >= n) return fail(KVC_ERR_INVALID, "kv_cache_set_split: form %d outside [0, %d)", form, n);
   h->split = form;
   return KVC_OK;
@@ -653,7 +653,7 @@ int kv_cache_autotune(kvc_handle h, const void* q, const void* k_cur, const void
   if (reps < 1) return fail(KVC_ERR_INVALID, "kv_cache_autotune: reps = %d < 1", reps);
   if (!q || !k_cur || !v_cur || !o) return fail(KVC_ERR_INVALID, "kv_cache_autotune: NULL q, k_cur, v_cur or o");
   const int n = config_count(h);
-  const int n_split = h->kv_dtype == KVC_KV_FP8 ? 2 : 4;
+  const int n_split = h->kv_dtype == KVC_KV_FP8 ? 2 : 5;
   const int before = h->config, before_split = h->split;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {

@@ -59,17 +59,30 @@ def test_fp8_config_many_units(D, cfg):
     run_stream(spec, [0, 3], rows=rows, config=cfg)
 
 
-@pytest.mark.parametrize("kv_dtype,form", [("bf16", 1), ("bf16", 2), ("bf16", 3), ("fp8", 1)])
+@pytest.mark.parametrize("kv_dtype,form", [("bf16", 1), ("bf16", 2), ("bf16", 3), ("bf16", 4), ("fp8", 1)])
 def test_split_forms(kv_dtype, form):
     """Each split form of a partly filled last round (whole units, aligned key
-    slices, one range per slot) against the oracle, on a stream whose units
-    fill more than one round."""
+    slices, one range per slot, whole heads with equal query tiles) against
+    the oracle, on a stream whose units fill more than one round."""
     from block_causal_kv_amd import KVCache
     spec = synthetic.small_spec("split%d_%s" % (form, kv_dtype), n_chunks=4, chunk_tokens=1104, cond_len=64,
                                 heads=96, head_dim=128, window=2, seed=55 + form, kv_dtype=kv_dtype)
     rows = np.array(sorted(set(range(0, 1104, 41)) | set(range(1094, 1104))))
     say("split form %d, %s" % (form, kv_dtype))
     run_stream(spec, [0, 3], rows=rows, split=form)
+
+
+def test_whole_heads_form_slices_the_last_head():
+    """Split form 4 on a shape where it slices: 24 heads of 11 equal query
+    tiles (237 rows, T = 2600) on 256 compute units put two whole heads on
+    each XCD and cut the tiles of the third into aligned key halves, which
+    the merge kernel combines; rows around every tile boundary compared."""
+    spec = synthetic.small_spec("whole_heads", n_chunks=4, chunk_tokens=2600, cond_len=64, heads=24, head_dim=128,
+                                window=2, seed=59)
+    edges = [r for b in range(237, 2600, 237) for r in (b - 1, b)]
+    rows = np.array(sorted(set(range(0, 2600, 53)) | set(edges) | set(range(2590, 2600))))
+    say("split form 4, 24 heads x 11 tiles")
+    run_stream(spec, [0, 3], rows=rows, split=4)
 
 
 def test_config_table_and_autotune():
@@ -97,7 +110,7 @@ def test_config_table_and_autotune():
     assert 0 <= best < 5 and len(ms) == 5 and all(m > 0 for m in ms)
     assert ms[best] == min(ms) or (best == 0 and min(ms) >= 0.98 * ms[0])
     assert cache.config == best
-    assert 0 <= cache.split < 4
+    assert 0 <= cache.split < 5
     assert cache.query() == before
     # every configuration gives the same result up to rounding order
     outs = []
