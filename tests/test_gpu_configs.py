@@ -85,6 +85,15 @@ def test_whole_heads_form_slices_the_last_head():
     run_stream(spec, [0, 3], rows=rows, split=4)
 
 
+def test_whole_heads_form_falls_back_where_heads_do_not_divide():
+    """Split form 4 with 5 heads (not a multiple of the 8 XCDs) acts as the
+    cost model: parity on ragged chunks over several query tiles."""
+    spec = synthetic.small_spec("whole_heads_odd", n_chunks=5, chunk_tokens=300, cond_len=20, heads=5, head_dim=128,
+                                window=2, steps=2, clean_from_last_step=False, outlier_frac=0.01, seed=61)
+    say("split form 4, 5 heads")
+    run_stream(spec, range(spec.n_chunks), split=4)
+
+
 def test_config_table_and_autotune():
     import torch
     from block_causal_kv_amd import KVCache, KVCError, _lib
