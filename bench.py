@@ -514,13 +514,13 @@ def tune_table(args) -> int:
         cache.set_condition(dev_bf16(ck), dev_bf16(cv))
         for _ in range(spec.n_sink + spec.window):
             cache.append_chunk(kc, vc)
-        n_split = 2 if spec.kv_dtype == "fp8" else 5
+        forms = [0, 1, 4] if spec.kv_dtype == "fp8" else [0, 1, 2, 3, 4]
         cfgs = cache.configs()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         best = {}
         for rnd in range(3):  # best of three rounds per candidate
             for c in range(len(cfgs)):
-                for f in range(n_split):
+                for f in forms:
                     cache.config, cache.split = c, f
                     cache.attention(q, k, v, out=out)
                     e0.record()

@@ -51,6 +51,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "attention_common.h"
 #include "launch.h"
 
@@ -750,15 +752,29 @@ int launch_fp8(AttnArgs& a, int config, hipStream_t stream) {
   a.tiles = tiles;
   // split the units of a partly filled last round into key slices (as in the bf16 kernel)
   const int slots = a.num_cus;  // one workgroup per CU
-  const int rest = units % slots;
+  int rest = units % slots;
   int slices = 1;
-  double best = rest == 0 ? 0.0 : 1.0;
-  // (the workspace holds 2 x num_cus pieces of 8 waves)
-  for (int s = 2; s <= kMaxSlicesF8 && s <= tiles && rest * s <= 2 * slots; ++s) {
-    const double cost = (double)((rest * s + slots - 1) / slots) / s + 0.02 * s;
-    if (cost < best) {
-      best = cost;
-      slices = s;
+  const int hpx = a.H / 8, spx = slots / 8;
+  if (a.split == 4 && a.H % 8 == 0 && slots % 8 == 0 && a.q_tiles <= spx) {
+    // whole heads (as split form 4 of the bf16 kernel): equal query tiles; on
+    // each XCD the heads whose tiles fit one round of its slots run whole, the
+    // tiles of its other heads are cut into aligned key slices
+    a.q_rows = (a.Tq + a.q_tiles - 1) / a.q_tiles;
+    const int whole = std::min(hpx, spx / a.q_tiles);
+    rest = units - 8 * whole * a.q_tiles;
+    if (rest > 0) {
+      const int s = std::min(std::min(spx / ((hpx - whole) * a.q_tiles), tiles), kMaxSlicesF8);
+      if (s >= 2 && rest * s <= 2 * slots) slices = s;
+    }
+  } else {
+    double best = rest == 0 ? 0.0 : 1.0;
+    // (the workspace holds 2 x num_cus pieces of 8 waves)
+    for (int s = 2; s <= kMaxSlicesF8 && s <= tiles && rest * s <= 2 * slots; ++s) {
+      const double cost = (double)((rest * s + slots - 1) / slots) / s + 0.02 * s;
+      if (cost < best) {
+        best = cost;
+        slices = s;
+      }
     }
   }
   if (slices > 1 && a.ws_o != nullptr && a.split != 1) {

@@ -633,8 +633,10 @@ int kv_cache_get_config(kvc_handle h, int* out_id) {
 int kv_cache_set_split(kvc_handle h, int form) {
   g_last_error.clear();
   if (!h) return fail(KVC_ERR_INVALID, "kv_cache_set_split: handle is NULL");
-  const int n = h->kv_dtype == KVC_KV_FP8 ? 2 : 5;
-  if (form < 0 || form >= n) return fail(KVC_ERR_INVALID, "kv_cache_set_split: form %d outside [0, %d)", form, n);
+  const bool fp8 = h->kv_dtype == KVC_KV_FP8;
+  if (form < 0 || form > 4 || (fp8 && (form == 2 || form == 3)))
+    return fail(KVC_ERR_INVALID, "kv_cache_set_split: form %d is not one of %s", form,
+                fp8 ? "0, 1, 4 (fp8 caches)" : "0 .. 4");
   h->split = form;
   return KVC_OK;
 }
@@ -653,7 +655,10 @@ int kv_cache_autotune(kvc_handle h, const void* q, const void* k_cur, const void
   if (reps < 1) return fail(KVC_ERR_INVALID, "kv_cache_autotune: reps = %d < 1", reps);
   if (!q || !k_cur || !v_cur || !o) return fail(KVC_ERR_INVALID, "kv_cache_autotune: NULL q, k_cur, v_cur or o");
   const int n = config_count(h);
-  const int n_split = h->kv_dtype == KVC_KV_FP8 ? 2 : 5;
+  // split forms tried: every one for bf16; cost model, none and whole heads for fp8
+  static const int kForms[] = {0, 1, 2, 3, 4}, kFormsF8[] = {0, 1, 4};
+  const int* forms = h->kv_dtype == KVC_KV_FP8 ? kFormsF8 : kForms;
+  const int n_split = h->kv_dtype == KVC_KV_FP8 ? 3 : 5;
   const int before = h->config, before_split = h->split;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
@@ -670,7 +675,7 @@ int kv_cache_autotune(kvc_handle h, const void* q, const void* k_cur, const void
   for (int round = 0; round < kRounds && rc == KVC_OK; ++round) {
     for (int id = 0; id < nc && rc == KVC_OK; ++id) {
       h->config = id / n_split;
-      h->split = id % n_split;
+      h->split = forms[id % n_split];
       rc = sink_window_attention(h, q, k_cur, v_cur, o, nullptr, 0.f, stream);  // warm-up
       if (rc != KVC_OK) break;
       if (hipEventRecord(e0, (hipStream_t)stream) != hipSuccess) {
@@ -712,7 +717,7 @@ int kv_cache_autotune(kvc_handle h, const void* q, const void* k_cur, const void
     return rc;
   }
   h->config = best / n_split;
-  h->split = best % n_split;
+  h->split = forms[best % n_split];
   if (out_id) *out_id = h->config;
   return KVC_OK;
 }

@@ -308,8 +308,9 @@ int kvc_chunks_workspace_bytes(kvc_handle h, int n_chunks, size_t* out_bytes);
  *   heads whose tiles fit one round of an XCD's slots run whole and the other
  *   heads' tiles are cut into aligned key slices, so each head's K/V is
  *   streamed by one round's tiles (the least traffic past L2; where the heads
- *   do not divide over the 8 XCDs it acts as 0).  fp8 caches: 0 and 1.
- *   Pieces of a split unit are merged by a second kernel.  Errors: INVALID.
+ *   do not divide over the 8 XCDs it acts as 0).  fp8 caches: 0, 1 and 4.
+ *   Pieces of a split unit are merged by a second kernel.  Errors: INVALID
+ *   (a form outside these).
  * kv_cache_autotune - run sink_window_attention on these inputs (the cache's
  *   current contents: call it at the state to tune for, e.g. a full window)
  *   with every (configuration, split form): three rounds over them, each

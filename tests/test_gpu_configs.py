@@ -59,7 +59,8 @@ def test_fp8_config_many_units(D, cfg):
     run_stream(spec, [0, 3], rows=rows, config=cfg)
 
 
-@pytest.mark.parametrize("kv_dtype,form", [("bf16", 1), ("bf16", 2), ("bf16", 3), ("bf16", 4), ("fp8", 1)])
+@pytest.mark.parametrize("kv_dtype,form", [("bf16", 1), ("bf16", 2), ("bf16", 3), ("bf16", 4), ("fp8", 1),
+                                           ("fp8", 4)])
 def test_split_forms(kv_dtype, form):
     """Each split form of a partly filled last round (whole units, aligned key
     slices, one range per slot, whole heads with equal query tiles) against
@@ -72,16 +73,19 @@ def test_split_forms(kv_dtype, form):
     run_stream(spec, [0, 3], rows=rows, split=form)
 
 
-def test_whole_heads_form_slices_the_last_head():
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_whole_heads_form_slices_the_last_head(kv_dtype):
     """Split form 4 on a shape where it slices: 24 heads of 11 equal query
-    tiles (237 rows, T = 2600) on 256 compute units put two whole heads on
+    tiles (236 rows, T = 2592) on 256 compute units put two whole heads on
     each XCD and cut the tiles of the third into aligned key halves, which
     the merge kernel combines; rows around every tile boundary compared."""
-    spec = synthetic.small_spec("whole_heads", n_chunks=4, chunk_tokens=2600, cond_len=64, heads=24, head_dim=128,
-                                window=2, seed=59)
-    edges = [r for b in range(237, 2600, 237) for r in (b - 1, b)]
-    rows = np.array(sorted(set(range(0, 2600, 53)) | set(edges) | set(range(2590, 2600))))
-    say("split form 4, 24 heads x 11 tiles")
+    T = 2592
+    spec = synthetic.small_spec("whole_heads_" + kv_dtype, n_chunks=4, chunk_tokens=T, cond_len=64, heads=24,
+                                head_dim=128, window=2, seed=59, kv_dtype=kv_dtype)
+    q_rows = -(-T // 11)
+    edges = [r for b in range(q_rows, T, q_rows) for r in (b - 1, b)]
+    rows = np.array(sorted(set(range(0, T, 53)) | set(edges) | set(range(T - 10, T))))
+    say("split form 4, 24 heads x 11 tiles, " + kv_dtype)
     run_stream(spec, [0, 3], rows=rows, split=4)
 
 
@@ -134,6 +138,14 @@ def test_config_table_and_autotune():
     assert f8.configs() == [(8, 1), (8, 1)]
     with pytest.raises(KVCError):
         f8.config = 2
+    for form in (0, 1, 4):  # the split forms of fp8 caches
+        f8.split = form
+        assert f8.split == form
+    for form in (2, 3, 5, -1):
+        with pytest.raises(KVCError) as e:
+            f8.split = form
+        assert e.value.code == _lib.KVC_ERR_INVALID
+    assert f8.split == 4
     f8.close()
 
 
