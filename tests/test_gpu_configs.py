@@ -73,19 +73,19 @@ def test_split_forms(kv_dtype, form):
     run_stream(spec, [0, 3], rows=rows, split=form)
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
-def test_whole_heads_form_slices_the_last_head(kv_dtype):
+@pytest.mark.parametrize("kv_dtype,D", [("bf16", 128), ("fp8", 128), ("bf16", 64), ("fp8", 64)])
+def test_whole_heads_form_slices_the_last_head(kv_dtype, D):
     """Split form 4 on a shape where it slices: 24 heads of 11 equal query
     tiles (236 rows, T = 2592) on 256 compute units put two whole heads on
     each XCD and cut the tiles of the third into aligned key halves, which
     the merge kernel combines; rows around every tile boundary compared."""
     T = 2592
-    spec = synthetic.small_spec("whole_heads_" + kv_dtype, n_chunks=4, chunk_tokens=T, cond_len=64, heads=24,
-                                head_dim=128, window=2, seed=59, kv_dtype=kv_dtype)
+    spec = synthetic.small_spec("whole_heads_%s_d%d" % (kv_dtype, D), n_chunks=4, chunk_tokens=T, cond_len=64,
+                                heads=24, head_dim=D, window=2, seed=59, kv_dtype=kv_dtype)
     q_rows = -(-T // 11)
     edges = [r for b in range(q_rows, T, q_rows) for r in (b - 1, b)]
     rows = np.array(sorted(set(range(0, T, 53)) | set(edges) | set(range(T - 10, T))))
-    say("split form 4, 24 heads x 11 tiles, " + kv_dtype)
+    say("split form 4, 24 heads x 11 tiles, %s, D=%d" % (kv_dtype, D))
     run_stream(spec, [0, 3], rows=rows, split=4)
 
 
