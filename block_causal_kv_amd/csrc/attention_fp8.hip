@@ -37,10 +37,11 @@
 // tiles and a shorter last one), 64-key tiles loaded straight into LDS
 // (buffer_load ... lds), key-slice split of the last round (slices leave
 // partials that a second kernel merges), units grouped by XCD.  Two
-// schedules of the key-tile loop: ping-pong (the default; two wave groups in
-// alternate MFMA and softmax phases over four LDS buffers, see the kernel)
-// and lockstep (every wave in the same phase, two buffers, the next tile's
-// loads spread over the S^T MFMAs).
+// schedules of the key-tile loop: ping-pong (two wave groups in alternate
+// MFMA and softmax phases over four LDS buffers, see the kernel; the default
+// keeps one workgroup barrier per key tile, a configuration a barrier at
+// every phase) and lockstep (every wave in the same phase, two buffers, the
+// next tile's loads spread over the S^T MFMAs).
 //
 // Key order: K rows are read so that in S^T's accumulator lane half hf holds
 // keys kb*32 + 16*hf + r in register r (16 consecutive keys per 32-key
@@ -69,11 +70,13 @@ typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 // Schedules of the key-tile loop (see the kernel).
 constexpr int kF8Lockstep = 0;  // all waves in the same phase; two LDS buffers
 constexpr int kF8PingPong = 1;  // two wave groups in alternate phases; four LDS buffers
+constexpr int kF8PingPong1 = 2; // the ping-pong with one workgroup barrier per key tile
 
 template <int D, int SCHED_ = kF8PingPong>
 struct F8Cfg {
   static constexpr int SCHED = SCHED_;
-  static constexpr bool PP = SCHED == kF8PingPong;
+  static constexpr bool PP = SCHED == kF8PingPong || SCHED == kF8PingPong1;
+  static constexpr bool ONE_BAR = SCHED == kF8PingPong1;  // one barrier per key tile
   static constexpr int NBUF = PP ? 4 : 2;
   static constexpr int NW = 8;
   static constexpr int NT = NW * 64;
@@ -452,7 +455,7 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (grp == 1) __syncthreads();  // group B starts one phase late
+    if (!C::ONE_BAR && grp == 1) __syncthreads();  // group B starts one phase late
     Cursor ccur = cur;              // tile j
     f32x16 sacc[2];
     i32x8 pv;                       // P8 of tile j-1 (Y_{j-1} -> X_j)
@@ -593,10 +596,14 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
       return issued;
     };
     // barriers: group A waits for its own loads at the end of its Y phases,
-    // group B at the end of its X phases (both odd global phases)
+    // group B at the end of its X phases (both odd global phases).  With one
+    // barrier per key tile (ONE_BAR) only those are kept, as in the bf16
+    // kernel: barrier k follows A's Y_{k-1} and B's X_{k-1}; tile t, loaded
+    // in Y_{t-2} into the buffer of tile t-4 (last read in X_{t-3}, before
+    // barrier t-2), is complete at barrier t and read from X_t on.
     auto end_x = [&]() {
       if (grp == 1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      __syncthreads();
+      if (!C::ONE_BAR || grp == 1) __syncthreads();
     };
     auto end_y = [&](bool issued) {
       if (grp == 0) {
@@ -605,7 +612,7 @@ __global__ __launch_bounds__(512, 1) void attention_fp8_kernel(AttnArgs a) {
         else
           __builtin_amdgcn_s_waitcnt(0x0F70);
       }
-      __syncthreads();
+      if (!C::ONE_BAR || grp == 0) __syncthreads();
     };
     phase_x(std::true_type(), std::false_type(), 0);
     end_x();
@@ -738,7 +745,7 @@ constexpr int kMaxSlicesF8 = 8;
 
 // launch configurations: the schedule of the key-tile loop (8 waves, one
 // workgroup per CU in both)
-constexpr int kF8Cfg[] = {kF8PingPong, kF8Lockstep};
+constexpr int kF8Cfg[] = {kF8PingPong1, kF8Lockstep, kF8PingPong};
 constexpr int kF8Configs = sizeof(kF8Cfg) / sizeof(kF8Cfg[0]);
 
 template <int D>
@@ -793,6 +800,8 @@ int launch_fp8(AttnArgs& a, int config, hipStream_t stream) {
   if (a.ev_start != nullptr && hipEventRecord((hipEvent_t)a.ev_start, stream) != hipSuccess) return -1;
   if (kF8Cfg[config] == kF8PingPong)
     hipLaunchKernelGGL((attention_fp8_kernel<D, kF8PingPong>), dim3(grid), dim3(C::NT), 0, stream, a);
+  else if (kF8Cfg[config] == kF8PingPong1)
+    hipLaunchKernelGGL((attention_fp8_kernel<D, kF8PingPong1>), dim3(grid), dim3(C::NT), 0, stream, a);
   else
     hipLaunchKernelGGL((attention_fp8_kernel<D, kF8Lockstep>), dim3(grid), dim3(C::NT), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return -1;

@@ -283,9 +283,13 @@ int kvc_chunks_workspace_bytes(kvc_handle h, int n_chunks, size_t* out_bytes);
 /*
  * Launch configurations of the attention kernel (waves per workgroup x
  * workgroups resident per CU x schedule of the key-tile loop).  bf16 caches:
- * 0 8x1 ping-pong, 1 4x2 lockstep, 2 8x1 in-wave pipeline, 3 4x2 in-wave at
- * D = 128; 0 8x1 ping-pong, 1 4x2 lockstep, 2 4x3 lockstep, 3 8x1 in-wave,
- * 4 4x2 in-wave at D = 64.  fp8 caches: 0 8x1 ping-pong, 1 8x1 lockstep.
+ * 0 8x1 ping-pong with one workgroup barrier per key tile, 1 4x2 lockstep,
+ * 2 8x1 in-wave pipeline, 3 4x2 in-wave, 4 8x1 ping-pong with a barrier at
+ * every phase at D = 128; 0 8x1 ping-pong (one barrier per key tile), 1 4x2
+ * lockstep, 2 4x3 lockstep, 3 8x1 in-wave, 4 4x2 in-wave, 5 8x1 ping-pong
+ * (a barrier at every phase) at D = 64.  fp8 caches: 0 8x1 ping-pong (one
+ * barrier per key tile), 1 8x1 lockstep, 2 8x1 ping-pong (a barrier at every
+ * phase).
  * kv_cache_config_info reports waves and workgroups only (configurations
  * that differ in the schedule alone report the same pair).  Configuration 0
  * is the default.

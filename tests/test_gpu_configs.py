@@ -11,8 +11,8 @@ from test_gpu_chunks import run_chunks
 
 pytestmark = pytest.mark.gpu
 
-# (head dim, configuration id): D = 128 has 4 configurations, D = 64 has 5
-N_CONFIGS = {128: 4, 64: 5}
+# (head dim, configuration id): D = 128 has 5 configurations, D = 64 has 6
+N_CONFIGS = {128: 5, 64: 6}
 CASES = [(D, c) for D in (128, 64) for c in range(N_CONFIGS[D])]
 
 
@@ -35,8 +35,9 @@ def test_config_many_units(D, cfg):
     run_stream(spec, [0, 3], rows=rows, config=cfg)
 
 
-# fp8: configuration 0 is the ping-pong schedule, 1 the lockstep one
-F8_CASES = [(D, c) for D in (128, 64) for c in range(2)]
+# fp8: configuration 0 is the ping-pong schedule with one barrier per key
+# tile, 1 the lockstep one, 2 the ping-pong with a barrier at every phase
+F8_CASES = [(D, c) for D in (128, 64) for c in range(3)]
 
 
 @pytest.mark.parametrize("D,cfg", F8_CASES, ids=["fp8-d%d-c%d" % c for c in F8_CASES])
@@ -105,10 +106,10 @@ def test_config_table_and_autotune():
                                 window=2, seed=60)
     H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
     cache = KVCache(T, spec.window, spec.n_sink, spec.cond_len, H, D)
-    assert cache.configs() == [(8, 1), (4, 2), (4, 3), (8, 1), (4, 2)]
+    assert cache.configs() == [(8, 1), (4, 2), (4, 3), (8, 1), (4, 2), (8, 1)]
     assert cache.config == 0
     with pytest.raises(KVCError) as e:
-        cache.config = 5
+        cache.config = 6
     assert e.value.code == _lib.KVC_ERR_INVALID
     ck, cv = synthetic.cond_inputs(spec)
     cache.set_condition(to_dev(ck), to_dev(cv))
@@ -120,14 +121,14 @@ def test_config_table_and_autotune():
     before = cache.query()
     best, ms = cache.autotune(q, k, v, reps=3)
     say("autotune: config %d, ms %s" % (best, ms))
-    assert 0 <= best < 5 and len(ms) == 5 and all(m > 0 for m in ms)
+    assert 0 <= best < 6 and len(ms) == 6 and all(m > 0 for m in ms)
     assert ms[best] == min(ms) or (best == 0 and min(ms) >= 0.98 * ms[0])
     assert cache.config == best
     assert 0 <= cache.split < 5
     assert cache.query() == before
     # every configuration gives the same result up to rounding order
     outs = []
-    for i in range(5):
+    for i in range(6):
         cache.config = i
         outs.append(cache.attention(q, k, v).float())
     torch.cuda.synchronize()
@@ -135,9 +136,9 @@ def test_config_table_and_autotune():
         assert (o - outs[0]).abs().max().item() < 2e-2
     cache.close()
     f8 = KVCache(64, 2, 1, 16, 2, 128, "fp8")
-    assert f8.configs() == [(8, 1), (8, 1)]
+    assert f8.configs() == [(8, 1), (8, 1), (8, 1)]
     with pytest.raises(KVCError):
-        f8.config = 2
+        f8.config = 3
     for form in (0, 1, 4):  # the split forms of fp8 caches
         f8.split = form
         assert f8.split == form
@@ -149,7 +150,7 @@ def test_config_table_and_autotune():
     f8.close()
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
 def test_whole_stream_other_config(cfg):
     """The whole-stream form with the other configurations."""
     from block_causal_kv_amd import KVCache

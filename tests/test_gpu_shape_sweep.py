@@ -31,7 +31,7 @@ def _cases(n=32, seed=2024):
             Lc = Lc // 16 * 16
         W = int(rng.integers(1, 6))
         n_sink = int(rng.integers(0, 3))
-        configs = 2 if fp8 else (5 if D == 64 else 4)
+        configs = 3 if fp8 else (6 if D == 64 else 5)
         out.append(dict(name="sweep%d" % i, n_chunks=n_sink + W + 2, chunk_tokens=T, cond_len=Lc,
                         heads=int(rng.integers(1, 17)), head_dim=D, window=W, n_sink=n_sink,
                         seed=100 + i, outlier_frac=0.01, kv_dtype="fp8" if fp8 else "bf16",
