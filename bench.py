@@ -405,7 +405,7 @@ def measure_stream(spec: synthetic.StreamSpec, steps: int, warmup: int, n_sets: 
     """Time ``steps`` steady chunk-steps of ``spec`` (attention calls + clean
     append) after ``warmup`` untimed ones; inputs resident in HBM first."""
     import torch
-    from block_causal_kv_amd import KVCache
+    from block_causal_kv_amd import KVCache, trace_range
     H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
     dev = torch.device("cuda", 0)
 
@@ -427,6 +427,11 @@ def measure_stream(spec: synthetic.StreamSpec, steps: int, warmup: int, n_sets: 
     stream = torch.cuda.current_stream()
 
     def chunk_step(i, ev=None):
+        # a roctx range per chunk-step (rocprofv3 --marker-trace); warm-up steps named apart
+        with trace_range(("chunk-step %d" if ev is not None else "warm-up chunk-step %d") % i):
+            _chunk_step(i, ev)
+
+    def _chunk_step(i, ev):
         s = sets[i % len(sets)]
         for st in range(spec.steps):
             if ev is not None:

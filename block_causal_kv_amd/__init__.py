@@ -13,7 +13,7 @@ from typing import List, Optional, Tuple
 from . import _lib
 from ._lib import KVCError, check, load
 
-__all__ = ["KVCache", "SlotTable", "KVCError", "load"]
+__all__ = ["KVCache", "SlotTable", "KVCError", "load", "trace_range"]
 
 _DTYPES = {"bf16": _lib.KVC_KV_BF16, "fp8": _lib.KVC_KV_FP8}
 
@@ -22,6 +22,22 @@ def _stream_ptr(stream) -> Optional[int]:
     import torch
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
+
+
+class trace_range:
+    """Context manager: a named roctx range (``kvc_trace_push`` / ``kvc_trace_pop``)
+    around a block of calls, e.g. one chunk-step, for ``rocprofv3 --marker-trace``."""
+
+    def __init__(self, name: str):
+        self._name = name.encode()
+
+    def __enter__(self):
+        check(load().kvc_trace_push(self._name))
+        return self
+
+    def __exit__(self, *exc):
+        check(load().kvc_trace_pop())
+        return False
 
 
 class KVCache:

@@ -50,6 +50,8 @@ SIGNATURES = {
                                                C.c_void_p]),
     "kvc_chunks_workspace_bytes": (C.c_int, [C.c_void_p, C.c_int, C.POINTER(C.c_size_t)]),
     "kv_cache_time_kernel": (C.c_int, [C.c_void_p, C.c_void_p, C.c_void_p]),
+    "kvc_trace_push": (C.c_int, [C.c_char_p]),
+    "kvc_trace_pop": (C.c_int, []),
     "kv_cache_pool_view": (C.c_int, [C.c_void_p, C.POINTER(C.c_void_p), C.POINTER(C.c_void_p),
                                      C.POINTER(C.c_void_p), _I64P, _IP]),
     "kvc_table_create": (C.c_int, [C.c_int, C.c_int, C.POINTER(C.c_void_p)]),

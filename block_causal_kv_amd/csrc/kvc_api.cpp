@@ -3,6 +3,7 @@
 // Every check happens before anything is enqueued, and a failed call leaves
 // the cache state unchanged.
 #include <hip/hip_runtime_api.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <algorithm>
 #include <cmath>
@@ -22,6 +23,16 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// A roctx range around the work one entry point enqueues, so that a trace
+// taken with rocprofv3 --marker-trace groups each call's kernels under its
+// name (host-side markers: a function call each when no profiler listens).
+struct TraceRange {
+  explicit TraceRange(const char* name) { roctxRangePushA(name); }
+  ~TraceRange() { roctxRangePop(); }
+  TraceRange(const TraceRange&) = delete;
+  TraceRange& operator=(const TraceRange&) = delete;
+};
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -188,6 +199,7 @@ int poison_slot(kvc_cache* r, int slot) {
 // maxima come from the library's static scratch array instead of the cache.
 int attention_call(kvc_cache* h, int n_q, const void* q, const void* k_cur, const void* v_cur, void* o, float* lse,
                    float scale, void* stream, bool noalloc, const char* who) {
+  TraceRange trace(who);
   if (!q || !k_cur || !v_cur || !o) return fail(KVC_ERR_INVALID, "%s: NULL q, k_cur, v_cur or o", who);
   if (n_q < 1 || (int64_t)n_q * h->D * 2 > INT32_MAX || (int64_t)h->H * ((n_q + 255) / 256) > INT32_MAX)
     return fail(KVC_ERR_INVALID, "%s: %d query rows (need 1 .. 32-bit offsets)", who, n_q);
@@ -456,6 +468,7 @@ int kv_cache_layer(kvc_handle h, int layer, kvc_handle* out_view) {
 
 int kv_cache_write_chunk(kvc_handle h, const void* k, const void* v, void* stream) {
   g_last_error.clear();
+  TraceRange trace("kv_cache_write_chunk");
   if (!h) return fail(KVC_ERR_INVALID, "kv_cache_write_chunk: handle is NULL");
   if (!k || !v) return fail(KVC_ERR_INVALID, "kv_cache_write_chunk: NULL K or V");
   if (write_chunk(h, k, v, (hipStream_t)stream, nullptr, nullptr) != 0)
@@ -480,6 +493,7 @@ int kv_cache_append_commit(kvc_handle h, int64_t* out_chunk_id, int* out_slot, i
 
 int kv_cache_set_condition_rows(kvc_handle h, int n, const void* k_cond, const void* v_cond, void* stream) {
   g_last_error.clear();
+  TraceRange trace("kv_cache_set_condition");
   if (!h) return fail(KVC_ERR_INVALID, "kv_cache_set_condition_rows: handle is NULL");
   if (n < 0 || n > h->Lc)
     return fail(KVC_ERR_INVALID, "kv_cache_set_condition_rows: n = %d outside [0, %d]", n, h->Lc);
@@ -509,6 +523,7 @@ int kv_cache_set_condition(kvc_handle h, const void* k_cond, const void* v_cond,
 int kv_cache_append_chunk(kvc_handle h, const void* k, const void* v, void* stream,
                           int64_t* out_chunk_id, int* out_slot, int64_t* out_evicted) {
   g_last_error.clear();
+  TraceRange trace("kv_cache_append_chunk");
   if (!h) return fail(KVC_ERR_INVALID, "kv_cache_append_chunk: handle is NULL");
   if (h->root)
     return fail(KVC_ERR_STATE,
@@ -651,6 +666,7 @@ int kv_cache_get_split(kvc_handle h, int* out_form) {
 int kv_cache_autotune(kvc_handle h, const void* q, const void* k_cur, const void* v_cur, void* o, int reps,
                       void* stream, int* out_id, float* out_ms) {
   g_last_error.clear();
+  TraceRange trace("kv_cache_autotune");
   if (!h) return fail(KVC_ERR_INVALID, "kv_cache_autotune: handle is NULL");
   if (reps < 1) return fail(KVC_ERR_INVALID, "kv_cache_autotune: reps = %d < 1", reps);
   if (!q || !k_cur || !v_cur || !o) return fail(KVC_ERR_INVALID, "kv_cache_autotune: NULL q, k_cur, v_cur or o");
@@ -769,6 +785,7 @@ int sink_window_attention_chunks(kvc_handle h, int n_chunks, const void* q, cons
                                  void* o, float* lse, float scale, void* workspace, size_t workspace_bytes,
                                  void* stream) {
   g_last_error.clear();
+  TraceRange trace("sink_window_attention_chunks");
   if (!h) return fail(KVC_ERR_INVALID, "sink_window_attention_chunks: handle is NULL");
   if (h->kv_dtype != KVC_KV_BF16)
     return fail(KVC_ERR_UNSUPPORTED, "sink_window_attention_chunks: bf16 caches only");
@@ -827,6 +844,19 @@ int kv_cache_time_kernel(kvc_handle h, void* start_event, void* stop_event) {
     return fail(KVC_ERR_INVALID, "kv_cache_time_kernel: give both events or neither");
   h->time_start = start_event;
   h->time_stop = stop_event;
+  return KVC_OK;
+}
+
+int kvc_trace_push(const char* name) {
+  g_last_error.clear();
+  if (!name) return fail(KVC_ERR_INVALID, "kvc_trace_push: name is NULL");
+  roctxRangePushA(name);
+  return KVC_OK;
+}
+
+int kvc_trace_pop(void) {
+  g_last_error.clear();
+  roctxRangePop();
   return KVC_OK;
 }
 

@@ -66,6 +66,20 @@ int kv_cache_pool_view(kvc_handle h, const void** k_pool, const void** v_pool, c
  */
 int kv_cache_time_kernel(kvc_handle h, void* start_event, void* stop_event);
 
+/*
+ * kvc_trace_push / kvc_trace_pop - open and close a named roctx range on the
+ * calling thread, around a caller's unit of work (one chunk-step of a
+ * stream, say), so that a trace taken with `rocprofv3 --marker-trace` groups
+ * the kernels of that unit under the name.  Ranges nest; every entry point
+ * that enqueues GPU work (the attention calls, appends and chunk writes,
+ * condition writes, the whole-stream call, autotune) opens its own range,
+ * named after it, inside the caller's.  name is copied by the tracer; pops
+ * must match pushes.  Host-side markers only: nothing is enqueued.
+ * Measurement tooling.  Errors: INVALID (name NULL).
+ */
+int kvc_trace_push(const char* name);
+int kvc_trace_pop(void);
+
 #ifdef __cplusplus
 }
 #endif

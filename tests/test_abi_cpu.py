@@ -164,3 +164,16 @@ def test_evict_errors_leave_state_unchanged():
         t.evict(1)  # only the sink remains
     t.reset()
     assert t.query()["occupancy"] == 0 and t.query()["next_chunk_id"] == 0
+
+
+def test_trace_ranges_are_host_only():
+    """kvc_trace_push / kvc_trace_pop only mark the host timeline (roctx):
+    they nest, need no GPU and reject a NULL name."""
+    from block_causal_kv_amd import KVCError, _lib, trace_range
+    lib = _lib.load()
+    with trace_range("chunk-step 0"):
+        with trace_range("inner"):
+            pass
+    assert lib.kvc_trace_push(None) == _lib.KVC_ERR_INVALID
+    with pytest.raises(KVCError):
+        _lib.check(lib.kvc_trace_push(None))

@@ -23,7 +23,7 @@ def test_host_code_under_asan_and_ubsan(tmp_path):
            "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include"),
            os.path.join(csrc, "kvc_api.cpp"), os.path.join(csrc, "slot_table.cpp"),
            os.path.join(ROOT, "tests", "sanitize", "driver.cpp"), os.path.join(ROOT, "tests", "sanitize", "stubs.cpp"),
-           "-L" + os.path.join(ROCM, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-o", exe]
+           "-L" + os.path.join(ROCM, "lib"), "-lamdhip64", "-lrocprofiler-sdk-roctx", "-Wl,-rpath," + os.path.join(ROCM, "lib"), "-o", exe]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-4000:]
     env = dict(os.environ)
