@@ -401,9 +401,12 @@ def whole_stream(args) -> int:
 
 
 def measure_stream(spec: synthetic.StreamSpec, steps: int, warmup: int, n_sets: int, autotune: bool,
-                   split: int = -1) -> dict:
+                   split: int = -1, clean_pass: bool = False) -> dict:
     """Time ``steps`` steady chunk-steps of ``spec`` (attention calls + clean
-    append) after ``warmup`` untimed ones; inputs resident in HBM first."""
+    append) after ``warmup`` untimed ones; inputs resident in HBM first.
+    clean_pass: after the denoise calls, one more call whose current-chunk
+    K/V are the clean K/V that are then appended (the pass that produces the
+    cache's entries), its queries the first denoise step's."""
     import torch
     from block_causal_kv_amd import KVCache, trace_range
     H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
@@ -440,6 +443,8 @@ def measure_stream(spec: synthetic.StreamSpec, steps: int, warmup: int, n_sets: 
             cache.attention(s["q"][st], s["k"][st], s["v"][st], out=out, stream=stream)
             if ev is not None:
                 ev[1][st].record(stream)
+        if clean_pass:
+            cache.attention(s["q"][0], s["kc"], s["vc"], out=out, stream=stream)
         if ev is not None:
             ev[2].record(stream)
         cache.append_chunk(s["kc"], s["vc"], stream=stream)
@@ -645,6 +650,9 @@ def main() -> int:
                          "(one JSON line per shape) instead of the throughput line")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the fp8-cache run that the default 720p line reports beside the headline")
+    ap.add_argument("--clean-pass", action="store_true",
+                    help="each chunk-step also runs the clean pass: a third attention call whose current "
+                         "K/V are the clean K/V it then appends")
     ap.add_argument("--no-autotune", action="store_true",
                     help="keep the default launch configuration instead of timing each once before the run")
     ap.add_argument("--chunks", type=int, default=0,
@@ -679,12 +687,14 @@ def main() -> int:
         return whole_stream(args)
     spec = synthetic.SPECS[args.config]
     H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
-    m = measure_stream(spec, args.steps, args.warmup, args.sets, not args.no_autotune, args.split)
+    m = measure_stream(spec, args.steps, args.warmup, args.sets, not args.no_autotune, args.split,
+                       args.clean_pass)
+    calls = spec.steps + (1 if args.clean_pass else 0)
     stream, elapsed, kernel_cfg = m["stream"], m["elapsed"], m["kernel_cfg"]
     attn_ms, app_ms = m["attn_ms"], m["app_ms"]
     ms_step = elapsed * 1e3 / args.steps
     fl_call = flop_per_call(spec)
-    value = spec.steps * fl_call * args.steps / elapsed / 1e12
+    value = calls * fl_call * args.steps / elapsed / 1e12
     attn_avg = float(np.mean(attn_ms))
     kern_avg = float(np.mean(m["kernel_ms"]))  # the attention kernel alone (events around its launch)
     achieved = fl_call / (kern_avg * 1e-3) / 1e12
@@ -704,9 +714,11 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "fp8 e4m3 K/V, fp8 MFMA" if spec.kv_dtype == "fp8" else "bf16",
         "data": "synthetic (seeded N(0,1), bf16; 1% of K rows x8)",
-        "config": {"workload": workload_name(spec), "chunk_tokens": T, "cond_len": spec.cond_len,
+        "config": {"workload": workload_name(spec) + (" (+ the clean pass: a third call whose K/V are the "
+                                                      "appended clean K/V)" if args.clean_pass else ""),
+                   "chunk_tokens": T, "cond_len": spec.cond_len,
                    "heads": H, "head_dim": D, "window": spec.window, "n_sink": spec.n_sink,
-                   "kv_len": spec.steady_kv_len(), "calls_per_step": spec.steps,
+                   "kv_len": spec.steady_kv_len(), "calls_per_step": calls,
                    "input_sets": args.sets, "kernel_config": kernel_cfg},
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "attention_ms_per_call": round(attn_avg, 4),
@@ -727,7 +739,7 @@ def main() -> int:
         # which a few warm-up steps alone do not); reported beside it
         f8 = synthetic.SPECS["fp8"]
         n8 = args.steps
-        m8 = measure_stream(f8, n8, args.warmup, args.sets, not args.no_autotune)
+        m8 = measure_stream(f8, n8, args.warmup, args.sets, not args.no_autotune, -1, args.clean_pass)
         a8 = float(np.mean(m8["attn_ms"]))
         k8 = float(np.mean(m8["kernel_ms"]))
         fl8 = flop_per_call(f8)
