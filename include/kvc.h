@@ -230,8 +230,14 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
  * process ends, and its address is looked up on the first call on each device.
  * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
  * (other streams, other caches) race.  The maxima are cleared by a fill kernel
- * at each call.  Errors: INVALID, STATE, HIP, UNSUPPORTED (more than 256
- * compute units; an fp8 handle of more than 4096 heads).
+ * at each call, and the call keeps no per-call host state, so it can be
+ * captured into a HIP graph and replayed with new contents in its input
+ * buffers (after one call outside capture on the device, which looks up the
+ * array's address), as long as the cache's slot table does not change
+ * between capture and replay.  (The allocating fp8 call alternates two maxima
+ * buffers from the host, so a captured copy of it would not reset them.)
+ * Errors: INVALID, STATE, HIP, UNSUPPORTED (more than 256 compute units; an
+ * fp8 handle of more than 4096 heads).
  */
 int sink_window_attention_noalloc(kvc_handle h, const void* q, const void* k_cur, const void* v_cur, void* o,
                                   float* lse, float scale, void* stream);
