@@ -64,12 +64,11 @@ struct kvc_cache {
   size_t k_bytes = 0, v_bytes = 0;
   float* scales = nullptr;    // fp8: [2][L*H][blocks]: block 0 = condition, 1 + s = slot s, last = current
   int scale_tensor = 0;       // fp8: L * H * blocks (offset of the V scales)
-  // fp8: maxima scratch of the quantiser, one region per (call site, layer)
-  // so that quantisations of different sites or layers may overlap on
-  // different streams (see amax_region); each region holds two buffers used
-  // in turn, the one not in use cleared by the quantiser for the next call.
+  // fp8: partial-maxima scratch of the quantiser, one region per (call
+  // site, layer) so that quantisations of different sites or layers may
+  // overlap on different streams (see amax_region); every quantisation
+  // writes its region's partials before reading them.
   uint32_t* amax = nullptr;
-  std::vector<int> amax_turn;  // root: the buffer the next quantisation of each region uses
   int blocks() const { return n_sink + W + 2; }
   int num_cus = 0;
   float* ws_o = nullptr;   // attention workspace: partials of split query tiles
@@ -113,42 +112,26 @@ namespace {
 enum AmaxSite { kSiteAttention = 0, kSiteChunk = 1, kSiteCondition = 2, kSites = 3 };
 
 // Words of the maxima scratch of a cache of L layers x H heads: per site, L
-// per-layer regions of 2 x 2H words and one all-layer region of 2 x 2HL.
-size_t amax_words(int H, int L) { return (size_t)kSites * 8 * H * L; }
+// per-layer regions of P H words and one all-layer region of P HL words
+// (P = kAmaxWordsPerHead partial maxima per head).
+size_t amax_words(int H, int L) { return (size_t)kSites * 2 * kvc::kAmaxWordsPerHead * H * L; }
 
-// Region (and its turn counter index) of a quantisation through handle h.
-void amax_region(kvc_cache* h, int site, uint32_t** base, int* words, int* turn_idx) {
+// Region of a quantisation through handle h.
+uint32_t* amax_region(kvc_cache* h, int site) {
   kvc_cache* r = h->top();
-  const size_t H = r->H, L = r->layers;
-  size_t off = (size_t)site * 8 * H * L;
-  if (h->root) {
-    off += (size_t)h->layer * 4 * H;
-    *words = (int)(2 * H);
-    *turn_idx = site * ((int)L + 1) + h->layer;
-  } else {
-    off += L * 4 * H;
-    *words = (int)(2 * H * L);
-    *turn_idx = site * ((int)L + 1) + (int)L;
-  }
-  *base = r->amax + off;
+  const size_t H = r->H, L = r->layers, P = kvc::kAmaxWordsPerHead;
+  size_t off = (size_t)site * 2 * P * H * L;
+  off += h->root ? (size_t)h->layer * P * H : L * P * H;
+  return r->amax + off;
 }
 
 // fp8 cache: quantise K/V bf16 [H][rows][D] into pool rows [row0, row0 + rows) with scale block blk.
 int quantize_into(kvc_cache* h, const void* k, const void* v, int rows, int row0, int blk, int site,
                   hipStream_t st) {
-  kvc_cache* r = h->top();
-  uint32_t* base;
-  int n, ti;
-  amax_region(h, site, &base, &n, &ti);
-  int& turn = r->amax_turn[ti];
-  uint32_t* cur = base + (size_t)turn * n;
-  uint32_t* next = base + (size_t)(1 - turn) * n;
-  const int rc = kvc::launch_quantize_fp8((const uint16_t*)k, (const uint16_t*)v, h->heads_written(), rows, h->D,
-                                          cur, next, n, (uint8_t*)h->k_pool, h->spare_rows * h->D,
-                                          (uint8_t*)h->v_pool, h->spare_rows, row0, h->scales + blk,
-                                          h->scale_tensor, h->blocks(), st);
-  if (rc == 0) turn = 1 - turn;
-  return rc;
+  return kvc::launch_quantize_fp8((const uint16_t*)k, (const uint16_t*)v, h->heads_written(), rows, h->D,
+                                  amax_region(h, site), (uint8_t*)h->k_pool, h->spare_rows * h->D,
+                                  (uint8_t*)h->v_pool, h->spare_rows, row0, h->scales + blk, h->scale_tensor,
+                                  h->blocks(), st);
 }
 
 // bf16 cache: K rows copied to pool rows [row0, row0 + rows), V written transposed to columns row0...
@@ -211,8 +194,7 @@ int attention_call(kvc_cache* h, int n_q, const void* q, const void* k_cur, cons
   const bool fp8 = h->kv_dtype == KVC_KV_FP8;
   float* ws_o = h->ws_o;
   float* ws_ml = h->ws_ml;
-  uint32_t* amax_cur = nullptr;
-  uint32_t* amax_next = nullptr;
+  uint32_t* amax_part = nullptr;
   if (noalloc) {
     if (h->num_cus > kvc::kStaticScratchCUs)
       return fail(KVC_ERR_UNSUPPORTED, "%s: the device has %d compute units; the static scratch holds the split "
@@ -227,8 +209,7 @@ int attention_call(kvc_cache* h, int n_q, const void* q, const void* k_cur, cons
     uint8_t* b = (uint8_t*)base;
     ws_o = (float*)b;
     ws_ml = (float*)(b + kvc::kStaticWsOBytes);
-    amax_cur = (uint32_t*)(b + kvc::kStaticWsOBytes + kvc::kStaticWsMlBytes);
-    amax_next = amax_cur + 2 * (size_t)h->heads_written();
+    amax_part = (uint32_t*)(b + kvc::kStaticWsOBytes + kvc::kStaticWsMlBytes);
   }
   kvc::AttnArgs a;
   std::memset(&a, 0, sizeof a);
@@ -280,15 +261,11 @@ int attention_call(kvc_cache* h, int n_q, const void* q, const void* k_cur, cons
     a.scale_head = h->blocks();
     int rc;
     if (noalloc) {
-      // the maxima start at zero: cleared here by a fill kernel (the array
-      // keeps whatever the last call left)
-      const int n = 2 * h->heads_written();
-      rc = kvc::launch_fill_spans(amax_cur, 1, 0, 0, (int64_t)n * 4, 0, st);
-      if (rc == 0)
-        rc = kvc::launch_quantize_fp8((const uint16_t*)k_cur, (const uint16_t*)v_cur, h->heads_written(), h->T, h->D,
-                                      amax_cur, amax_next, n, (uint8_t*)h->k_pool, h->spare_rows * h->D,
-                                      (uint8_t*)h->v_pool, h->spare_rows, cur_row0, h->scales + n_slots + 1,
-                                      h->scale_tensor, h->blocks(), st);
+      // the partial maxima in the static array (each written before it is read)
+      rc = kvc::launch_quantize_fp8((const uint16_t*)k_cur, (const uint16_t*)v_cur, h->heads_written(), h->T, h->D,
+                                    amax_part, (uint8_t*)h->k_pool, h->spare_rows * h->D, (uint8_t*)h->v_pool,
+                                    h->spare_rows, cur_row0, h->scales + n_slots + 1, h->scale_tensor,
+                                    h->blocks(), st);
     } else {
       rc = quantize_into(h, k_cur, v_cur, h->T, cur_row0, n_slots + 1, kSiteAttention, st);
     }
@@ -378,14 +355,6 @@ int kv_cache_create_layers(int chunk_tokens, int window_w, int n_sink, int cond_
   e = hipMalloc(&c->k_pool, c->k_bytes);
   if (e == hipSuccess) e = hipMalloc(&c->v_pool, c->v_bytes);
   if (e == hipSuccess && fp8) e = hipMalloc(&c->scales, sizeof(float) * 2 * all_heads * c->blocks());
-  if (fp8) {
-    try {
-      c->amax_turn.assign((size_t)kSites * (layers + 1), 0);
-    } catch (...) {
-      delete c;
-      return fail(KVC_ERR_OOM, "kv_cache_create: host allocation failed");
-    }
-  }
   if (e == hipSuccess && fp8) e = hipMalloc(&c->amax, sizeof(uint32_t) * amax_words(heads, layers));
   if (e == hipSuccess && fp8) e = hipMemset(c->amax, 0, sizeof(uint32_t) * amax_words(heads, layers));
   if (e == hipSuccess && fp8) e = hipMemset(c->scales, 0, sizeof(float) * 2 * all_heads * c->blocks());

@@ -15,7 +15,7 @@ constexpr int kStaticScratchCUs = 256;
 constexpr int kStaticScratchHeads = 4096;
 constexpr size_t kStaticWsOBytes = (size_t)2 * kStaticScratchCUs * 8 * 4 * 16 * 64 * 4;  // 64 MiB
 constexpr size_t kStaticWsMlBytes = (size_t)2 * kStaticScratchCUs * 12 * 2 * 64 * 4;    // 1.5 MiB
-constexpr size_t kStaticAmaxBytes = (size_t)2 * 2 * kStaticScratchHeads * 4;             // 64 KiB
+constexpr size_t kStaticAmaxBytes = (size_t)2 * 16 * kStaticScratchHeads * 4;            // 512 KiB
 constexpr size_t kStaticScratchBytes = kStaticWsOBytes + kStaticWsMlBytes + kStaticAmaxBytes;
 
 // Arguments of one attention call.  Segments are pool row ranges of one head
@@ -131,14 +131,14 @@ int launch_attention_fp8(AttnArgs& a, int head_dim, int config, hipStream_t stre
 
 // Quantise K and V (bf16 [H][rows][D]) into E4M3 codes: K row-major into
 // k_dst[h*k_head + (row0 + r)*D + d], V transposed into vt_dst[(h*D + d)*vt_rows + row0 + r];
-// scales[t*scale_tensor + h*scale_head] <- amax/448 (t = 0 K, 1 V).  amax_bits:
-// 2*H words of scratch.
-// amax_bits: zeroed [2][H] scratch for this call; amax_next: the other buffer
-// ([n_amax] words), cleared here for the next call.
-int launch_quantize_fp8(const uint16_t* k, const uint16_t* v, int H, int rows, int D, uint32_t* amax_bits,
-                        uint32_t* amax_next, int n_amax, uint8_t* k_dst, int64_t k_head, uint8_t* vt_dst,
-                        int64_t vt_rows, int row0, float* scales, int scale_tensor, int scale_head,
-                        hipStream_t stream);
+// scales[t*scale_tensor + h*scale_head] <- amax/448 (t = 0 K, 1 V).  partial:
+// kAmaxWordsPerHead * H words of scratch, every one written by the call
+// before it is read (nothing needs clearing, and nothing carries over).
+constexpr int kAmaxBlocks = 16;                     // partial maxima per (head, tensor)
+constexpr int kAmaxWordsPerHead = 2 * kAmaxBlocks;  // K and V
+int launch_quantize_fp8(const uint16_t* k, const uint16_t* v, int H, int rows, int D, uint32_t* partial,
+                        uint8_t* k_dst, int64_t k_head, uint8_t* vt_dst, int64_t vt_rows, int row0, float* scales,
+                        int scale_tensor, int scale_head, hipStream_t stream);
 
 // Measurement probes (csrc/probes.hip).
 int launch_mfma_probe(float* sink, int blocks, int iters, hipStream_t stream);

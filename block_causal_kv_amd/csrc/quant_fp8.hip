@@ -10,11 +10,13 @@
 //
 // K codes are stored row-major [H][rows][D]; V codes are stored transposed,
 // [H][D][rows] (the PV product reads V^T, and the transposition is free here).
-// Two kernels: a per-head absolute maximum (atomic max on the float's bits,
-// which order like the values for non-negative floats), then the quantising
-// write, which also records the scale (the second pass over the input mostly
-// hits the cache: a chunk's K and V are tens of MB).  The maxima live in one of two
-// buffers used in turn; each quantisation clears the other one for the next.
+// Two kernels: partial absolute maxima (each block of the first stores the
+// maximum of its share of a head's K or V in a word of its own), then the
+// quantising write, whose blocks each take the maximum of their head's
+// partials and which records the scale (the second pass over the input mostly
+// hits the cache: a chunk's K and V are tens of MB).  Every partial is written
+// by every call, so the scratch carries nothing from one call to the next:
+// no clearing, no atomics, and a captured call replays correctly.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -52,16 +54,15 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
-// amax of K (tensor 0) and V (tensor 1) per head: grid (blocks, H, 2) with
-// at most kAmaxBlocks blocks per (head, tensor), each thread kAmaxLoads
-// independent 16-byte loads per step.  Atomics on one address serialise
-// (about a quarter of a microsecond each on this device), so a (head, tensor)
-// gets few, large blocks rather than many small ones.
+// Partial amax of K (tensor 0) and V (tensor 1) per head: grid (blocks, H, 2)
+// with at most kAmaxBlocks blocks per (head, tensor), each thread kAmaxLoads
+// independent 16-byte loads per step; block x of (head h, tensor t) stores its
+// maximum's bits (non-negative floats order like their bits) at
+// partial[(t * H + h) * kAmaxBlocks + x].
 constexpr int kAmaxLoads = 16;
-constexpr int kAmaxBlocks = 16;
 __global__ __launch_bounds__(256) void amax_bf16_kernel(const uint16_t* __restrict__ k,
                                                         const uint16_t* __restrict__ v, int n16,
-                                                        uint32_t* __restrict__ amax_bits) {
+                                                        uint32_t* __restrict__ partial) {
   const uint4* src = (const uint4*)((blockIdx.z == 0 ? k : v) + (int64_t)blockIdx.y * n16 * 8);
   float m = 0.f;
   for (int i0 = blockIdx.x * (256 * kAmaxLoads) + threadIdx.x; i0 < n16; i0 += gridDim.x * (256 * kAmaxLoads)) {
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(256) void amax_bf16_kernel(const uint16_t* __restri
   __syncthreads();
   if (threadIdx.x == 0) {
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    atomicMax(&amax_bits[blockIdx.z * gridDim.y + blockIdx.y], __float_as_uint(m));
+    partial[(blockIdx.z * gridDim.y + blockIdx.y) * kAmaxBlocks + blockIdx.x] = __float_as_uint(m);
   }
 }
 
@@ -98,24 +99,24 @@ __global__ __launch_bounds__(256) void amax_bf16_kernel(const uint16_t* __restri
 template <int D>
 __global__ __launch_bounds__(D * 2) void quantize_bf16_kernel(const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v, int rows,
-                                                              const uint32_t* __restrict__ amax_bits,
+                                                              const uint32_t* __restrict__ partial, int n_part,
                                                               uint8_t* __restrict__ k_dst, int64_t k_head,
                                                               uint8_t* __restrict__ vt_dst, int64_t vt_rows,
                                                               int row0, float* __restrict__ scales,
-                                                              int scale_tensor, int scale_head,
-                                                              uint32_t* __restrict__ amax_next, int n_next) {
+                                                              int scale_tensor, int scale_head) {
   constexpr int TR = 64;     // rows per block
   constexpr int NC = D / 8;  // 8-dim pieces per row
   constexpr int NT = NC * (TR / 4);
-  // the other amax buffer, used by the next quantisation, starts at zero
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
-    for (int i = threadIdx.x; i < n_next; i += NT) amax_next[i] = 0u;
   __shared__ __attribute__((aligned(16))) uint8_t tile[D * TR];
   const int tensor = blockIdx.z;
   const int h = blockIdx.y;
   const int r0 = blockIdx.x * TR;
   const int nr = min(TR, rows - r0);  // rows of this tile
-  const float amax = __uint_as_float(amax_bits[tensor * gridDim.y + h]);
+  // the head's maximum: the largest of the amax kernel's partials (exact)
+  const uint32_t* pm = partial + (tensor * gridDim.y + h) * kAmaxBlocks;
+  uint32_t amax_b = 0u;
+  for (int i = 0; i < n_part; ++i) amax_b = max(amax_b, pm[i]);
+  const float amax = __uint_as_float(amax_b);
   const float scale = amax > 0.f ? amax / 448.0f : 1.0f;  // correctly rounded float32 division
   if (blockIdx.x == 0 && threadIdx.x == 0) scales[tensor * scale_tensor + h * scale_head] = scale;
   const Divider div(scale);
@@ -180,21 +181,20 @@ __global__ __launch_bounds__(D * 2) void quantize_bf16_kernel(const uint16_t* __
 
 }  // namespace
 
-int launch_quantize_fp8(const uint16_t* k, const uint16_t* v, int H, int rows, int D, uint32_t* amax_bits,
-                        uint32_t* amax_next, int n_amax, uint8_t* k_dst, int64_t k_head, uint8_t* vt_dst,
-                        int64_t vt_rows, int row0, float* scales, int scale_tensor, int scale_head,
-                        hipStream_t stream) {
+int launch_quantize_fp8(const uint16_t* k, const uint16_t* v, int H, int rows, int D, uint32_t* partial,
+                        uint8_t* k_dst, int64_t k_head, uint8_t* vt_dst, int64_t vt_rows, int row0, float* scales,
+                        int scale_tensor, int scale_head, hipStream_t stream) {
   if (rows <= 0) return 0;
   const int n16 = rows * D / 8;  // 16-byte pieces per head (D in {64, 128})
   const int blocks = std::min((n16 + 256 * kAmaxLoads - 1) / (256 * kAmaxLoads), kAmaxBlocks);
-  hipLaunchKernelGGL(amax_bf16_kernel, dim3(blocks, H, 2), dim3(256), 0, stream, k, v, n16, amax_bits);
+  hipLaunchKernelGGL(amax_bf16_kernel, dim3(blocks, H, 2), dim3(256), 0, stream, k, v, n16, partial);
   const dim3 grid((rows + 63) / 64, H, 2);
   if (D == 128)
-    hipLaunchKernelGGL(quantize_bf16_kernel<128>, grid, dim3(256), 0, stream, k, v, rows, amax_bits, k_dst,
-                       k_head, vt_dst, vt_rows, row0, scales, scale_tensor, scale_head, amax_next, n_amax);
+    hipLaunchKernelGGL(quantize_bf16_kernel<128>, grid, dim3(256), 0, stream, k, v, rows, partial, blocks, k_dst,
+                       k_head, vt_dst, vt_rows, row0, scales, scale_tensor, scale_head);
   else if (D == 64)
-    hipLaunchKernelGGL(quantize_bf16_kernel<64>, grid, dim3(128), 0, stream, k, v, rows, amax_bits, k_dst,
-                       k_head, vt_dst, vt_rows, row0, scales, scale_tensor, scale_head, amax_next, n_amax);
+    hipLaunchKernelGGL(quantize_bf16_kernel<64>, grid, dim3(128), 0, stream, k, v, rows, partial, blocks, k_dst,
+                       k_head, vt_dst, vt_rows, row0, scales, scale_tensor, scale_head);
   else
     return -2;
   return hipGetLastError() == hipSuccess ? 0 : -1;

@@ -224,18 +224,17 @@ int sink_window_attention(kvc_handle h, const void* q, const void* k_cur, const 
  * taken from a static device array of the library instead of memory the cache
  * allocated at create.  The call allocates nothing, HIP or otherwise.
  *   q, k_cur, v_cur, o, lse, scale, stream: as sink_window_attention.
- * The array (64 MiB + 1.5 MiB + 64 KiB) holds the split
+ * The array (64 MiB + 1.5 MiB + 512 KiB) holds the split
  * workspace of a device of at most 256 compute units and the fp8 maxima of at
  * most 4096 heads; every GPU the library runs on keeps its own copy until the
  * process ends, and its address is looked up on the first call on each device.
  * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
- * (other streams, other caches) race.  The maxima are cleared by a fill kernel
- * at each call, and the call keeps no per-call host state, so it can be
- * captured into a HIP graph and replayed with new contents in its input
- * buffers (after one call outside capture on the device, which looks up the
- * array's address), as long as the cache's slot table does not change
- * between capture and replay.  (The allocating fp8 call alternates two maxima
- * buffers from the host, so a captured copy of it would not reset them.)
+ * (other streams, other caches) race.  Every scratch word a call reads (the
+ * fp8 quantiser's partial maxima included) is written by that call first, and
+ * the call keeps no per-call host state, so it can be captured into a HIP
+ * graph and replayed with new contents in its input buffers (after one call
+ * outside capture on the device, which looks up the array's address), as long
+ * as the cache's slot table does not change between capture and replay.
  * Errors: INVALID, STATE, HIP, UNSUPPORTED (more than 256 compute units; an
  * fp8 handle of more than 4096 heads).
  */

@@ -36,8 +36,8 @@ int attention_fp8_configs(int* waves, int* wgs, int* sched, int cap) {
   return 2;
 }
 int launch_attention_fp8(AttnArgs&, int, int, hipStream_t) { return -1; }
-int launch_quantize_fp8(const uint16_t*, const uint16_t*, int, int, int, uint32_t*, uint32_t*, int, uint8_t*, int64_t,
-                        uint8_t*, int64_t, int, float*, int, int, hipStream_t) {
+int launch_quantize_fp8(const uint16_t*, const uint16_t*, int, int, int, uint32_t*, uint8_t*, int64_t, uint8_t*,
+                        int64_t, int, float*, int, int, hipStream_t) {
   return -1;
 }
 int launch_mfma_probe(float*, int, int, hipStream_t) { return -1; }

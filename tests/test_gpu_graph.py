@@ -1,11 +1,12 @@
-"""sink_window_attention_noalloc under HIP graph capture: the call for callers
-that cannot allocate (code under graph capture is one) captured once with
-torch.cuda.graph, then replayed with new contents in its input buffers, with
-the program's own eager calls and synchronisations between the replays.
-Every replay must equal the eager call on the same inputs bit for bit (the
-same kernels run), for a bf16 and an fp8 cache; the fp8 call's maxima start
-from a fill kernel in every replay, so no replay sees the last one's.  A
-small stream is also checked against the oracle."""
+"""Attention calls under HIP graph capture: sink_window_attention_noalloc (the
+call for callers that cannot allocate; code under graph capture is one) and
+sink_window_attention, each captured once with torch.cuda.graph and then
+replayed with new contents in its input buffers, with the program's own eager
+calls and synchronisations between the replays.  Every replay must equal the
+eager call on the same inputs bit for bit (the same kernels run), for a bf16
+and an fp8 cache: every scratch word a call reads, the fp8 quantiser's
+partial maxima included, is written by that call first, so no replay sees
+the last one's.  A small stream is also checked against the oracle."""
 import numpy as np
 import pytest
 
@@ -16,7 +17,7 @@ from streams import BF16_MAX_ABS, BF16_REL_L2, errors, from_dev, say, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def _replays(spec, n_sets, check_oracle):
+def _replays(spec, n_sets, check_oracle, noalloc=True):
     import torch
     from block_causal_kv_amd import KVCache
     H, T, D = spec.heads, spec.chunk_tokens, spec.head_dim
@@ -36,12 +37,13 @@ def _replays(spec, n_sets, check_oracle):
     lse_s = torch.empty((H, T), dtype=torch.float32, device="cuda")
     ref = torch.empty_like(q_s)
     lse_ref = torch.empty_like(lse_s)
+    call = cache.attention_noalloc if noalloc else cache.attention
     # an eager call first: the library looks up its static scratch address once
-    cache.attention_noalloc(q_s, k_s, v_s, out=out_s, lse=lse_s)
+    call(q_s, k_s, v_s, out=out_s, lse=lse_s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        cache.attention_noalloc(q_s, k_s, v_s, out=out_s, lse=lse_s)
+        call(q_s, k_s, v_s, out=out_s, lse=lse_s)
     torch.cuda.synchronize()
     for r in range(2 * n_sets):
         i = r % n_sets
@@ -50,7 +52,7 @@ def _replays(spec, n_sets, check_oracle):
         k_s.copy_(k)
         v_s.copy_(v)
         out_s.fill_(float("nan"))
-        cache.attention_noalloc(q, k, v, out=ref, lse=lse_ref)  # eager work between the replays
+        call(q, k, v, out=ref, lse=lse_ref)  # eager work between the replays
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
@@ -70,14 +72,15 @@ def _replays(spec, n_sets, check_oracle):
     cache.close()
 
 
+@pytest.mark.parametrize("entry", ["noalloc", "alloc"])
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
-def test_noalloc_graph_replays(kv_dtype):
+def test_graph_replays(kv_dtype, entry):
     # 720p-sized call: the last round of query tiles is split, so the merge
     # kernel is part of the graph
-    big = synthetic.small_spec("graph-big-" + kv_dtype, n_chunks=8, chunk_tokens=3600, cond_len=256, heads=24,
-                               head_dim=128, window=4, seed=95, outlier_frac=0.01, kv_dtype=kv_dtype)
-    say("graph replays", kv_dtype)
-    _replays(big, 3, check_oracle=False)
+    big = synthetic.small_spec("graph-big-%s-%s" % (kv_dtype, entry), n_chunks=8, chunk_tokens=3600, cond_len=256,
+                               heads=24, head_dim=128, window=4, seed=95, outlier_frac=0.01, kv_dtype=kv_dtype)
+    say("graph replays", kv_dtype, entry)
+    _replays(big, 3, check_oracle=False, noalloc=entry == "noalloc")
 
 
 def test_noalloc_graph_replays_small_against_oracle():
