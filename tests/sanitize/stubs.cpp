@@ -28,12 +28,13 @@ int launch_transpose_v_bf16(const uint16_t*, uint16_t*, int, int, int, int64_t, 
 int launch_fill_spans(void*, int64_t, int64_t, int64_t, int64_t, uint16_t, hipStream_t) { return -1; }
 int static_scratch(void**, size_t*) { return -1; }
 int attention_fp8_configs(int* waves, int* wgs, int* sched, int cap) {
-  for (int i = 0; i < 2 && i < cap; ++i) {
+  static const int kSched[3] = {2, 0, 1};  // as the library's fp8 configurations
+  for (int i = 0; i < 3 && i < cap; ++i) {
     if (waves) waves[i] = 8;
     if (wgs) wgs[i] = 1;
-    if (sched) sched[i] = 1 - i;
+    if (sched) sched[i] = kSched[i];
   }
-  return 2;
+  return 3;
 }
 int launch_attention_fp8(AttnArgs&, int, int, hipStream_t) { return -1; }
 int launch_quantize_fp8(const uint16_t*, const uint16_t*, int, int, int, uint32_t*, uint8_t*, int64_t, uint8_t*,
